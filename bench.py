@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Default workload: single-layer paged decode at Qwen3-0.6B shape (16 query heads, 8 KV
+heads, head_dim 128, bf16), batch 64, context lengths uniform in [512, 4096], block
+size 16, physical blocks shuffled over a pool of need + 10 %.  One step is the hot
+path of one layer: pa_write_kv of the 64 new tokens, then pa_decode (split-K partial
+pass + merge pass), all inputs resident in HBM.
+
+Prints one JSON line.  ``value`` is the whole-step throughput in GB/s of algorithmic
+HBM traffic; ``roofline`` describes the decode call (both of its kernels) timed with
+HIP events on the stream it runs on; ``cpu_baseline`` is the CPU oracle timed on the
+host on the same inputs.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+
+WORKLOADS = ("qwen3_decode_b64", "long_decode_b8", "shared_prefix_decode_b128",
+             "chunked_prefill_r16")
+
+
+def make_workload(name: str, seed: int):
+    from paged_kv_cache_73_amd import workloads as W
+    return {"qwen3_decode_b64": W.qwen3_decode, "long_decode_b8": W.long_decode,
+            "shared_prefix_decode_b128": W.shared_prefix_decode,
+            "chunked_prefill_r16": W.chunked_prefill}[name](seed=seed)
+
+
+def decode_bytes(w, plan) -> int:
+    """Algorithmic HBM bytes of one pa_decode: K and V of every key read once
+    (2*Hkv*d*elem per sequence-token), q read and out written (Hq*d*elem each per
+    sequence), and one 4-byte table entry per page."""
+    e = w.elem_bytes
+    keys = sum(plan.seqlens_k)
+    pages = sum(-(-n // w.block_size) for n in plan.seqlens_k)
+    return keys * 2 * w.kv_dim * e + w.batch * 2 * w.num_heads * w.head_dim * e + pages * 4
+
+
+def write_bytes(w, plan) -> int:
+    """pa_write_kv reads each new K and V row and writes it once; copy-on-write
+    copies read and write whole blocks of K and V."""
+    e = w.elem_bytes
+    rows = len(plan.new_slots)
+    blk = w.block_size * w.kv_dim * e
+    return rows * 4 * w.kv_dim * e + len(plan.copies) * 4 * blk
+
+
+def prefill_flops(w, plan) -> float:
+    """4*d*Hq per visible (query, key) pair; causal pairs of request i with q_i queries
+    after c_i cached keys: q_i*c_i + q_i(q_i+1)/2."""
+    tot = 0
+    for qn, c in zip(w.new, w.cached):
+        tot += qn * c + qn * (qn + 1) // 2
+    return 4.0 * w.head_dim * w.num_heads * tot
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str, workload: str):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current source of the kernel; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float, max_rows=None) -> dict:
+    """The CPU oracle (gather + two-pass softmax in float64), one thread, on the same
+    inputs, repeated for about ``seconds``."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as OA
+    from tests.harness import oracle_run, storage
+
+    o = oracle_run(w, attention=False)
+    q = storage(w.q, w.dtype)
+    table = np.asarray(o.plan.tables)
+    with threadpool_limits(limits=1):
+        if w.kind == "decode":
+            rows = list(range(w.batch if max_rows is None else min(max_rows, w.batch)))
+            seq = [o.plan.seqlens_k[r] for r in rows]
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                OA.decode(q[rows], o.k_pool, o.v_pool, table[rows], seq, w.scale, w.dtype)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    break
+            keys = sum(seq) * reps
+            e = w.elem_bytes
+            nbytes = (keys * 2 * w.kv_dim * e + reps * len(rows) * 2 * w.num_heads * w.head_dim * e)
+            return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                    "seq_tokens_per_s": keys / el,
+                    "sample": f"{len(rows)} of {w.batch} sequences x {reps} passes "
+                              f"({el:.1f} s, float64 gather + two-pass softmax, 1 thread)"}
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            OA.prefill_varlen(q, o.k_pool, o.v_pool, o.plan.cu_q, o.plan.cu_k, table, w.scale,
+                              w.causal, w.dtype)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        fl = prefill_flops(w, o.plan) * reps
+        return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                "sample": f"all {w.batch} requests x {reps} passes ({el:.1f} s, 1 thread)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_decode_b64", choices=WORKLOADS)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="decode launches timed after flushing the caches (reported apart)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) "
+              "is not supported: there is no multi-GPU path to measure.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_73_amd import _native
+    if not os.path.exists(_native.LIB_PATH):
+        from paged_kv_cache_73_amd import build as B
+        B.build()
+    from paged_kv_cache_73_amd import runner as R
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = make_workload(args.workload, args.seed)
+    r = R.setup(w, dev)
+    P = args.partition_tokens
+    if w.kind == "decode":
+        R.ensure_workspace(w, r, P)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        R.write(w, r)
+        R.attend(w, r, P)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        R.write(w, r)
+        a.record(stream)
+        R.attend(w, r, P)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    attn_mean_ms = sum(attn_ms) / len(attn_ms)
+    attn_median_ms = attn_ms[len(attn_ms) // 2]
+    ms_per_step = wall * 1e3 / args.steps
+
+    # the same attention call after evicting L2 and the MALL by reading 1 GiB (a read
+    # leaves clean lines, so the timed call pays no write-backs)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(args.cold_reps):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        R.attend(w, r, P)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    cold_median_ms = sorted(cold)[len(cold) // 2] if cold else None
+
+    plan = r.plan
+    kernel_src = os.path.join(ROOT, "paged_kv_cache_73_amd", "csrc",
+                              "decode.hip" if w.kind == "decode" else "prefill.hip")
+    cfg = {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
+           "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+           "num_blocks": w.num_blocks, "seed": args.seed}
+    if w.kind == "decode":
+        dbytes = decode_bytes(w, plan)
+        step_bytes = dbytes + write_bytes(w, plan)
+        keys = sum(plan.seqlens_k)
+        achieved = dbytes / (attn_mean_ms * 1e-3) / 1e9
+        cfg.update({"context_min": min(plan.seqlens_k), "context_max": max(plan.seqlens_k),
+                    "sum_context": keys, "partition_tokens": P or "auto"})
+        line = {
+            "metric": "decode-attn HBM GB/s (% of peak) + seq-tokens/s, Qwen3-0.6B shape B=64",
+            "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
+            "unit": "GB/s",
+            "pct_of_hbm_peak": 100.0 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "seq_tokens_per_s": keys / (ms_per_step * 1e-3),
+        }
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kernel_src, w.name),
+                "kernel": "pa_decode (decode_partial_kernel + decode_merge_kernel)",
+                "algorithmic_bytes_per_launch": dbytes,
+                "launch_us_mean": attn_mean_ms * 1e3, "launch_us_median": attn_median_ms * 1e3,
+                "cold_launch_us_median": None if cold_median_ms is None else cold_median_ms * 1e3,
+                "cold_achieved": None if not cold_median_ms else dbytes / (cold_median_ms * 1e-3) / 1e9}
+    else:
+        fl = prefill_flops(w, plan)
+        achieved = fl / (attn_mean_ms * 1e-3) / 1e12
+        cfg.update({"sum_q": sum(w.new), "sum_k": sum(plan.seqlens_k), "causal": w.causal})
+        line = {"metric": "varlen paged prefill TFLOP/s (% of bf16 MFMA peak)",
+                "value": fl / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                "traffic": load_traffic(kernel_src, w.name), "kernel": "pa_prefill_varlen",
+                "algorithmic_flops_per_launch": fl, "launch_us_mean": attn_mean_ms * 1e3,
+                "launch_us_median": attn_median_ms * 1e3,
+                "cold_launch_us_median": None if cold_median_ms is None else cold_median_ms * 1e3}
+    line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                 "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+                 "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+                 "config": cfg, "roofline": roof})
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

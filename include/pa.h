@@ -1,0 +1,236 @@
+/*
+ * pa.h -- C ABI of libpa, paged attention over a block-table-indexed KV cache for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [PA11]  "Paged attention 与 online softmax" (dilfish.github.io, chapter 11):
+ *           §11.1 block table / address / pool size, §11.2 block-merge online
+ *           softmax, §11.3 sharing, copy-on-write, reference counts.
+ *   [NANO]  "结合nanovllm的FlashAttention和PagedAttention主要原理概述"
+ *           (meredith2328.github.io): 题目2 online softmax, 题目3 FlashAttention tiles,
+ *           题目4 on-demand blocks, 题目5 block table, 题目6 prefix reference counts.
+ *   [QWEN]  "从零开始写Qwen3（六）PagedAttention" (mlqm.cn reprint): 分页自注意力的改进
+ *           (address rule), packed 模式, fast-attn 库的使用 (varlen prefill and decode
+ *           call signatures), 自己来实现 (slot_mapping write).
+ *   [HFPA]  "Sayfalı dikkat" (Hugging Face transformers docs, Turkish): varlen path
+ *           (Değişken uzunluklu yol) and decode path (Çözme yolu) with examples.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - KV pools: two caller-owned device buffers, K and V, each laid out
+ *   [num_blocks][block_size][num_kv_heads][head_dim], row-major, head_dim fastest
+ *   ([PA11] §11.1: the K vector of (phys, slot) starts at phys*B*kvDim + slot*kvDim,
+ *   kvDim = num_kv_heads*head_dim).  Element type pa_dtype.
+ * - A logical token p of sequence s lives in physical block table[s][p / B] at slot
+ *   p % B ([PA11] §11.1, [NANO] 题目5); its flat slot index is table[s][p/B]*B + p%B
+ *   ([QWEN] 分页自注意力的改进).
+ * - Block tables: int32 [batch][max_blocks_per_seq] on the device, unassigned entries
+ *   -1 ([HFPA] decode example).  Entries outside [0, num_blocks) within a sequence's
+ *   length are a caller error; the kernels never dereference them: such blocks are
+ *   treated as masked (their keys take no part), keeping every access in bounds.
+ * - Query head h uses KV head h / (num_heads / num_kv_heads) (grouped-query attention).
+ * - Every device call enqueues asynchronously on `stream` (a hipStream_t; NULL is the
+ *   default stream), never synchronises, never allocates device memory and keeps no
+ *   state between calls.  All pointers named "device" must be device memory that
+ *   stays valid until the enqueued work completes.
+ * - Every call returns a pa_status.  Scalar arguments are validated on the host
+ *   before anything is launched; on error nothing is enqueued.  A failed launch
+ *   returns PA_ERR_HIP.  The contents of device metadata (tables, lengths, slots)
+ *   are not validated by the device calls (that would need a synchronisation);
+ *   the pa_validate_* functions check host copies of them.
+ * - Supported: dtype F32 or BF16, head_dim 64 or 128, block_size 16 or 32,
+ *   num_heads / num_kv_heads in {1, 2, 4, 8}, num_kv_heads <= 64.  Other shapes
+ *   return PA_ERR_UNSUPPORTED.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = -1,   /* null pointer, negative size, inconsistent shapes  */
+    PA_ERR_UNSUPPORTED = -2,   /* valid but not implemented (dtype, head_dim, ...)  */
+    PA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required        */
+    PA_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed        */
+    PA_ERR_OUT_OF_BLOCKS = -5, /* block manager: not enough free blocks             */
+    PA_ERR_REFCOUNT = -6,      /* block manager: reference count would go below 0   */
+    PA_ERR_METADATA = -7       /* pa_validate_*: metadata contents are inconsistent */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Describes the two caller-owned device pools; see the conventions above. */
+typedef struct {
+    int32_t dtype;         /* pa_dtype                                           */
+    int32_t num_blocks;    /* physical blocks in each pool                       */
+    int32_t block_size;    /* B, tokens per block                                */
+    int32_t num_kv_heads;  /* Hkv                                                */
+    int32_t head_dim;      /* d                                                  */
+    void* k_cache;         /* device, [num_blocks][B][Hkv][d]                    */
+    void* v_cache;         /* device, same shape                                 */
+} pa_kv_pool;
+
+/* Human-readable name of a pa_status value (static string, never NULL). */
+const char* pa_status_str(int status);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int32_t pa_abi_version(void);
+
+/* ---------------------------------------------------------------------------------
+ * KV write ([QWEN] 自己来实现: one program per new token copies its HIDDEN_DIM K and V
+ * values to row slot_mapping[n] of the cache and returns early for a negative slot).
+ *
+ * k_new, v_new: device, [num_tokens][Hkv][d], same dtype as the pool.
+ * slot_mapping: device int32 [num_tokens]; slot = phys*B + offset.  Negative slots are
+ *   skipped; slots >= num_blocks*B are skipped too (out of range).  Two tokens with
+ *   the same non-negative slot is a caller error (the surviving row is unspecified).
+ * The copy is bit-exact.  num_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------------- */
+int pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Copy-on-write data step ([PA11] §11.3: before writing into a shared block, allocate a
+ * new block and copy the old contents there).  For i < num_pairs, block dst[i] of both
+ * pools receives a bit-exact copy of block src[i].  src, dst: device int32 arrays; a
+ * pair with an id outside [0, num_blocks) is skipped.  dst blocks must be distinct and
+ * must not appear in src.  The pairs come from pa_bm_prepare_write.
+ * ------------------------------------------------------------------------------- */
+int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src, const int32_t* dst,
+                   int32_t num_pairs, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Decode: one query token per sequence ([HFPA] Çözme yolu; [QWEN] fast-attn 库的使用,
+ * flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens, block_table, scale)).
+ *
+ * out, q: device, [batch][num_heads][d], pool dtype.  out = softmax(scale * K q) V over
+ *   the first seqlens_k[b] keys of sequence b, read through block_table row b.
+ *   The KV of the current token must already be written (pa_write_kv), and
+ *   seqlens_k counts it.  A sequence with no key gets a zero row.
+ * block_table: device int32 [batch][max_blocks_per_seq].
+ * seqlens_k: device int32 [batch], 0 <= seqlens_k[b] <= min(max_seqlen_k,
+ *   max_blocks_per_seq*B).  Keys beyond max_blocks_per_seq*B are never read.
+ * max_seqlen_k: host bound on seqlens_k, sizes the grid and the workspace.
+ * partition_tokens: split-K partition length (a multiple of B; 0 picks a default).
+ *   Keys are cut into partitions processed by different workgroups; each yields an
+ *   online-softmax state (m, l, o) and a second kernel merges them with the [PA11]
+ *   §11.2 rule.  Sequences with one partition are finished by the first kernel.
+ * workspace: device scratch of at least pa_decode_workspace_bytes(...) bytes (may be
+ *   NULL when that is 0); its contents need no initialisation.
+ * ------------------------------------------------------------------------------- */
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_seqlen_k, int32_t partition_tokens,
+                                 int32_t block_size);
+
+int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+              int32_t num_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
+              const int32_t* seqlens_k, int32_t max_seqlen_k, float softmax_scale,
+              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Varlen (packed) prefill with a paged cache ([QWEN] fast-attn 库的使用:
+ * flash_attn_varlen_func(q, k_cache, v_cache, max_seqlen_q, cu_seqlens_q, max_seqlen_k,
+ * cu_seqlens_k, scale, causal, block_table); [HFPA] Değişken uzunluklu yol).
+ *
+ * q, out: device, [total_q][num_heads][d] with total_q = cu_seqlens_q[batch]; BF16
+ *   pools only (F32 returns PA_ERR_UNSUPPORTED).
+ * cu_seqlens_q, cu_seqlens_k: device int32 [batch+1], non-decreasing from 0.  Request
+ *   i owns query rows [cu_q[i], cu_q[i+1]) and k_len = cu_k[i+1]-cu_k[i] keys, read
+ *   through block_table row i (only the differences of cu_k are used; the new tokens'
+ *   K/V must already be written).  With c = k_len - q_len cached tokens, query row t
+ *   sees keys j <= c + t when causal != 0 (bottom-right alignment), all k_len keys
+ *   otherwise.  A row that sees no key gets zeros.
+ * max_seqlen_q, max_seqlen_k: host bounds on the per-request lengths (grid sizing).
+ * ------------------------------------------------------------------------------- */
+int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                      int32_t num_heads, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                      int32_t max_seqlen_k, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, float softmax_scale, int32_t causal,
+                      void* stream);
+
+/* =================================================================================
+ * Host-side block manager and metadata builders (no device memory, single-threaded;
+ * every pointer below is host memory).
+ * ================================================================================= */
+
+/* Reference-counted free stack of physical block ids ([PA11] §11.3: refs[p] counts the
+ * block tables or prefix holders pointing at p; allocation sets 1, sharing adds 1,
+ * release subtracts 1, and a block returns to the free stack only at 0; [NANO] 题目6:
+ * free blocks are handed out 0, 1, 2, ... and a freed block is the next one reused). */
+typedef struct pa_bm pa_bm;
+
+/* initial_order: NULL for 0,1,2,..., else a permutation of [0, num_blocks) giving the
+ * order in which blocks are first handed out.  *out receives the new manager. */
+int pa_bm_create(int32_t num_blocks, const int32_t* initial_order, pa_bm** out);
+void pa_bm_destroy(pa_bm* bm);
+int32_t pa_bm_num_free(const pa_bm* bm);
+/* Reference count of `block` (>= 0), or PA_ERR_INVALID_ARG for an id out of range. */
+int pa_bm_refcount(const pa_bm* bm, int32_t block);
+/* Copies the free stack, next-to-be-handed-out first, into out[0 .. *count). */
+int pa_bm_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity, int32_t* count);
+/* Takes n blocks (refs = 1 each) into ids_out; all or nothing (PA_ERR_OUT_OF_BLOCKS). */
+int pa_bm_alloc(pa_bm* bm, int32_t n, int32_t* ids_out);
+int pa_bm_incref(pa_bm* bm, int32_t block);
+/* Drops one reference; at 0 the block goes on top of the free stack. */
+int pa_bm_decref(pa_bm* bm, int32_t block);
+/* End of a request: drops one reference per assigned entry, walking the row in
+ * reverse ([NANO] 题目6, deallocation). */
+int pa_bm_release_table(pa_bm* bm, const int32_t* row, int32_t width);
+/* Sharing: row_out = row, with one more reference on every assigned entry. */
+int pa_bm_share(pa_bm* bm, const int32_t* row, int32_t width, int32_t* row_out);
+/* Makes logical positions [start, start+count) of a table row writable: unassigned
+ * entries get a new block ([NANO] 题目4, on-demand growth); entries whose block is
+ * shared (refs > 1) get copy-on-write ([PA11] §11.3): a new block replaces the entry,
+ * the old block loses this row's reference, and (src=old, dst=new) is appended to
+ * cow_src/cow_dst (at most cow_capacity pairs; *num_cow receives the count).  All or
+ * nothing: on PA_ERR_OUT_OF_BLOCKS neither the row nor the manager changes. */
+int pa_bm_prepare_write(pa_bm* bm, int32_t block_size, int32_t* row, int32_t width,
+                        int32_t start, int32_t count, int32_t* cow_src, int32_t* cow_dst,
+                        int32_t cow_capacity, int32_t* num_cow);
+
+/* slots_out[i] = table[seq[i]][pos[i] / B] * B + pos[i] % B, or -1 when that entry is
+ * unassigned ([QWEN] 自己来实现: slot_mapping is computed once and reused by every
+ * layer).  table: [*][width]; PA_ERR_INVALID_ARG when pos[i]/B >= width or seq[i] < 0. */
+int pa_build_slot_mapping(const int32_t* table, int32_t width, int32_t block_size,
+                          const int32_t* seq, const int32_t* pos, int32_t n,
+                          int32_t* slots_out);
+/* cu_out[0] = 0, cu_out[i+1] = cu_out[i] + lengths[i] ([HFPA] varlen example);
+ * *max_out = max length (0 for batch 0). */
+int pa_build_cu_seqlens(const int32_t* lengths, int32_t batch, int32_t* cu_out,
+                        int32_t* max_out);
+
+/* Pool bytes for K and V together ([PA11] §11.1: numBlocks * B * 2 * kvDim * elem). */
+int64_t pa_pool_bytes(int32_t num_blocks, int32_t block_size, int32_t kv_dim,
+                      int32_t elem_bytes);
+
+/* Checks host copies of decode metadata: 0 <= seqlens[b] <= min(max_seqlen_k,
+ * width*B) and every table entry a sequence's length reaches is in [0, num_blocks).
+ * Returns PA_OK or PA_ERR_METADATA (*bad_index receives the first offending batch
+ * row, may be NULL). */
+int pa_validate_decode(const int32_t* table, int32_t batch, int32_t width,
+                       const int32_t* seqlens, int32_t max_seqlen_k, int32_t num_blocks,
+                       int32_t block_size, int32_t* bad_index);
+/* Checks host copies of varlen metadata: cu arrays start at 0 and do not decrease,
+ * q_len <= max_seqlen_q, k_len <= max_seqlen_k and k_len <= width*B, and table entries
+ * reached are in range.  Note k_len < q_len is allowed (its first rows see nothing). */
+int pa_validate_varlen(const int32_t* table, int32_t batch, int32_t width,
+                       const int32_t* cu_q, const int32_t* cu_k, int32_t max_seqlen_q,
+                       int32_t max_seqlen_k, int32_t num_blocks, int32_t block_size,
+                       int32_t* bad_index);
+/* Checks a slot mapping: every non-negative slot < num_blocks*B and no slot twice. */
+int pa_validate_slots(const int32_t* slots, int32_t n, int32_t num_blocks,
+                      int32_t block_size, int32_t* bad_index);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,429 @@
+// Paged decode attention: one query token per sequence, grouped-query heads,
+// split-K over partitions of the context with an online-softmax merge.
+//
+// What it computes ("Sayfalı dikkat", Çözme yolu; "从零开始写Qwen3（六）PagedAttention",
+// fast-attn 库的使用): out[b,h] = softmax(scale * K_b q[b,h]) V_b over the first
+// seqlens[b] keys of sequence b, key p read from physical block table[b][p/B] at slot
+// p mod B ("Paged attention 与 online softmax" §11.1).
+//
+// How (gfx950):
+// * Pass 1, one workgroup per (sequence, partition, group of KV heads), one wave per
+//   KV head.  A wave walks the pages of its partition; a page of one head is B rows of
+//   d*elem bytes.  Lanes take consecutive 16-byte pieces of a row (LPR lanes cover a
+//   row, so one load instruction covers 64/LPR whole rows = 1 KiB of the page), which
+//   keeps every wave load fully coalesced; the workgroup as a whole streams whole
+//   pages (B*Hkv*d contiguous elements) of K and then V.
+// * The query heads that share the KV head (GQA group of G) are all served from the
+//   same registers, so each K/V byte is read from HBM once.
+// * QK dot products: each lane multiplies its 16 bytes, then DPP row permutations sum
+//   the LPR lanes of a row.  Each lane keeps its own online-softmax state (m, l, o)
+//   over the rows it loaded ("Paged attention 与 online softmax" §11.2: blocks of keys
+//   can be folded in any grouping and merged), so P*V needs no cross-lane traffic.
+//   At the end of the partition the row groups are merged with the same rule.
+// * Softmax runs in base 2 (q is prescaled by scale*log2(e)), using the hardware exp2.
+// * The next page's K and V are loaded before the current page is consumed, so two
+//   pages per wave are in flight.
+// * Pass 2 merges the partitions' (m, l, o) of every (sequence, head) with the boxed
+//   rule of §11.2 and normalises.  A sequence that fits in one partition is finished
+//   by pass 1 and skipped by pass 2.
+// * Masked keys (past the sequence end, or in a block whose id is outside
+//   [0, num_blocks)) are selected away, never multiplied by 0, and a block with an
+//   invalid id is never loaded.
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace pa {
+
+template <typename T, int D, int BS>
+struct PageShape {
+    static constexpr int kElemBytes = Storage<T>::kBytes;
+    static constexpr int kRowBytes = D * kElemBytes;
+    static constexpr int kLanesPerRow = kRowBytes / 16;      // LPR
+    static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
+    static constexpr int kLoads = BS / kRowsPerLoad;         // load instructions per page
+    static constexpr int kElems = 16 / kElemBytes;           // values per lane per load
+    static_assert(kLanesPerRow >= 1 && kLanesPerRow <= kWave, "row size");
+    static_assert(BS % kRowsPerLoad == 0, "block size vs rows per load");
+};
+
+// Online-softmax update of one lane's state with NS new base-2 scores.
+template <int NS, int E>
+__device__ __forceinline__ void fold(float& m, float& l, float (&o)[E], const float (&s)[NS],
+                                     const float (&v)[NS][E]) {
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < NS; ++i) mx = fmaxf(mx, s[i]);
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing seen yet
+    const float corr = __builtin_amdgcn_exp2f(m - m_use);
+    float p[NS];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+        psum += p[i];
+    }
+    l = l * corr + psum;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        float acc = o[e] * corr;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) acc += p[i] * v[i][e];
+        o[e] = acc;
+    }
+    m = m_new;
+}
+
+// Merge (m, l, o) with the state held by the lane `off` positions away (xor).
+template <int E>
+__device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[E], int off) {
+    const float m_o = __shfl_xor(m, off);
+    const float l_o = __shfl_xor(l, off);
+    const float m_new = fmaxf(m, m_o);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float a = __builtin_amdgcn_exp2f(m - m_use);
+    const float b = __builtin_amdgcn_exp2f(m_o - m_use);
+    l = l * a + l_o * b;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float o_o = __shfl_xor(o[e], off);
+        o[e] = o[e] * a + o_o * b;
+    }
+    m = m_new;
+}
+
+template <typename T, int D, int BS, int G>
+__global__ __launch_bounds__(512) void decode_partial_kernel(
+    const T* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
+    T* __restrict__ out, float* __restrict__ o_part, float* __restrict__ ml_part,
+    int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks, int32_t max_blocks,
+    int32_t max_parts, int32_t part_pages, float qscale) {
+    using S = PageShape<T, D, BS>;
+    constexpr int LPR = S::kLanesPerRow;
+    constexpr int RPL = S::kRowsPerLoad;
+    constexpr int NL = S::kLoads;
+    constexpr int E = S::kElems;
+
+    const int lane = threadIdx.x % kWave;
+    const int heads_per_wg = blockDim.x / kWave;
+    const int hkv = blockIdx.z * heads_per_wg + threadIdx.x / kWave;
+    const int b = blockIdx.y;
+    const int part = blockIdx.x;
+    const int r0 = lane / LPR;  // first row of this lane within a load
+    const int c = lane % LPR;   // 16-byte piece of the row
+
+    const int32_t cap = max_blocks * BS;
+    const int32_t seqlen = min(max(seqlens[b], 0), cap);
+    const int32_t part_tokens = part_pages * BS;
+    const int32_t n_parts = max(1, (seqlen + part_tokens - 1) / part_tokens);
+    if (part >= n_parts) return;  // uniform over the workgroup
+    const int32_t t_end = min(seqlen, (part + 1) * part_tokens);
+    const int32_t pg0 = part * part_pages;
+    int32_t pg1 = (t_end + BS - 1) / BS;
+
+    // query heads of this KV head, this lane's E dims, prescaled to base 2
+    float qv[G][E];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int h = hkv * G + g;
+        const uint4 w = *reinterpret_cast<const uint4*>(
+            q + (static_cast<int64_t>(b) * num_heads + h) * D + c * E);
+        widen(w, qv[g], T{});
+#pragma unroll
+        for (int e = 0; e < E; ++e) qv[g][e] *= qscale;
+    }
+
+    float m[G], l[G], o[G][E];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[g][e] = 0.f;
+    }
+
+    const int64_t page_bytes = static_cast<int64_t>(BS) * num_kv_heads * S::kRowBytes;
+    // byte offset of this lane's first piece inside a page, and the step between loads
+    const int32_t lane_off = (r0 * num_kv_heads + hkv) * S::kRowBytes + c * 16;
+    const int32_t load_step = RPL * num_kv_heads * S::kRowBytes;
+    const int32_t* table_row = block_table + static_cast<int64_t>(b) * max_blocks;
+
+    // Consume one page of K/V already in registers.  A page whose block id is outside
+    // [0, num_blocks) was loaded from block 0 instead and is masked entirely.
+    auto consume = [&](int32_t id, int32_t tok0, const uint4 (&kb)[NL], const uint4 (&vb)[NL]) {
+        const bool valid = id >= 0 && id < num_blocks;
+        float s[G][NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            float kf[E];
+            widen(kb[j], kf, T{});
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc += qv[g][e] * kf[e];
+                s[g][j] = group_sum<LPR>(acc);
+            }
+        }
+        float vf[NL][E];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) widen(vb[j], vf[j], T{});
+        if (!valid || tok0 + BS > t_end) {
+            // last page of the sequence (or an unassigned block): select the rows to keep
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const bool ok = valid && tok0 + r0 + j * RPL < t_end;
+#pragma unroll
+                for (int g = 0; g < G; ++g) s[g][j] = ok ? s[g][j] : -INFINITY;
+#pragma unroll
+                for (int e = 0; e < E; ++e) vf[j][e] = ok ? vf[j][e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) fold<NL, E>(m[g], l[g], o[g], s[g], vf);
+    };
+    // Issue the loads of one page (always in bounds: invalid ids read block 0).
+    auto load_page = [&](int32_t id, uint4 (&kd)[NL], uint4 (&vd)[NL]) {
+        const uint64_t base = static_cast<uint64_t>(static_cast<uint32_t>(
+                                  (id >= 0 && id < num_blocks) ? id : 0)) * page_bytes;
+        const char* kp = k_cache + base;
+        const char* vp = v_cache + base;
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            kd[j] = *reinterpret_cast<const uint4*>(kp + static_cast<uint32_t>(lane_off + j * load_step));
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            vd[j] = *reinterpret_cast<const uint4*>(vp + static_cast<uint32_t>(lane_off + j * load_step));
+    };
+
+    if (num_blocks <= 0) pg1 = pg0;  // nothing can be read
+    for (int32_t pc = pg0; pc < pg1; pc += kWave) {
+        const int np = min(kWave, pg1 - pc);
+        const int32_t my_id = (lane < np) ? table_row[pc + lane] : -1;
+        // ping-pong: while one page is consumed the next one is in flight
+        uint4 ka[NL], va[NL], kb[NL], vb[NL];
+        int32_t id_a = __builtin_amdgcn_readlane(my_id, 0);
+        load_page(id_a, ka, va);
+        int i = 0;
+        for (; i + 2 < np; i += 2) {
+            const int32_t id_b = __builtin_amdgcn_readlane(my_id, i + 1);
+            load_page(id_b, kb, vb);
+            consume(id_a, (pc + i) * BS, ka, va);
+            id_a = __builtin_amdgcn_readlane(my_id, i + 2);
+            load_page(id_a, ka, va);
+            consume(id_b, (pc + i + 1) * BS, kb, vb);
+        }
+        if (i + 1 < np) {
+            const int32_t id_b = __builtin_amdgcn_readlane(my_id, i + 1);
+            load_page(id_b, kb, vb);
+            consume(id_a, (pc + i) * BS, ka, va);
+            consume(id_b, (pc + i + 1) * BS, kb, vb);
+        } else {
+            consume(id_a, (pc + i) * BS, ka, va);
+        }
+    }
+
+    // merge the row groups (lanes with the same piece c)
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) merge_xor<E>(m[g], l[g], o[g], off);
+    }
+    if (r0 != 0) return;
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int h = hkv * G + g;
+        const int64_t bh = static_cast<int64_t>(b) * num_heads + h;
+        if (n_parts == 1) {
+            float r[E];
+            const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) r[e] = o[g][e] * inv;
+            *reinterpret_cast<uint4*>(out + bh * D + c * E) = narrow(r, T{});
+        } else {
+            float* op = o_part + (bh * max_parts + part) * D + c * E;
+#pragma unroll
+            for (int e = 0; e < E; e += 4)
+                *reinterpret_cast<float4*>(op + e) = make_float4(o[g][e], o[g][e + 1], o[g][e + 2], o[g][e + 3]);
+            if (c == 0)
+                *reinterpret_cast<float2*>(ml_part + (bh * max_parts + part) * 2) = make_float2(m[g], l[g]);
+        }
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWave) void decode_merge_kernel(
+    const int32_t* __restrict__ seqlens, const float* __restrict__ o_part,
+    const float* __restrict__ ml_part, T* __restrict__ out, int32_t num_heads, int32_t cap,
+    int32_t max_parts, int32_t part_tokens) {
+    constexpr int PER = D / kWave;  // dims per lane
+    const int h = blockIdx.x;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int32_t seqlen = min(max(seqlens[b], 0), cap);
+    const int32_t n_parts = max(1, (seqlen + part_tokens - 1) / part_tokens);
+    if (n_parts == 1) return;  // finished by pass 1
+    const int64_t bh = static_cast<int64_t>(b) * num_heads + h;
+    const float2* ml = reinterpret_cast<const float2*>(ml_part) + bh * max_parts;
+    float M = -INFINITY;
+    for (int p = 0; p < n_parts; ++p) M = fmaxf(M, ml[p].x);
+    float L = 0.f, O[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) O[k] = 0.f;
+    if (M != -INFINITY) {
+        for (int p = 0; p < n_parts; ++p) {
+            const float2 st = ml[p];
+            const float w = __builtin_amdgcn_exp2f(st.x - M);
+            L += w * st.y;
+            const float* op = o_part + (bh * max_parts + p) * D;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) O[k] += w * op[lane + k * kWave];
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const float r = O[k] * inv;
+        if constexpr (sizeof(T) == 4) {
+            out[bh * D + lane + k * kWave] = r;
+        } else {
+            reinterpret_cast<uint16_t*>(out)[bh * D + lane + k * kWave] = to_bf16_bits(r);
+        }
+    }
+}
+
+constexpr int kDefaultPartitionTokens = 256;
+
+inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size) {
+    int32_t p = partition_tokens > 0 ? partition_tokens : kDefaultPartitionTokens;
+    if (p < block_size) p = block_size;
+    return p;
+}
+
+template <typename T, int D, int BS, int G>
+int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                  int32_t num_heads, const int32_t* table, int32_t max_blocks,
+                  const int32_t* seqlens, int32_t max_parts, int32_t part_tokens, float scale,
+                  float* o_part, float* ml_part, hipStream_t stream) {
+    const int hkv = pool->num_kv_heads;
+    int per_wg = 8;
+    while (hkv % per_wg != 0) per_wg >>= 1;
+    const dim3 grid(max_parts, batch, hkv / per_wg);
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, BS, G>), grid, dim3(per_wg * kWave), 0, stream,
+                       static_cast<const T*>(q), static_cast<const char*>(pool->k_cache),
+                       static_cast<const char*>(pool->v_cache), table, seqlens,
+                       static_cast<T*>(out), o_part, ml_part, num_heads, hkv, pool->num_blocks,
+                       max_blocks, max_parts, part_tokens / BS, scale * kLog2e);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    if (max_parts > 1) {
+        hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(num_heads, batch), dim3(kWave), 0,
+                           stream, seqlens, o_part, ml_part, static_cast<T*>(out), num_heads,
+                           max_blocks * BS, max_parts, part_tokens);
+    }
+    return launch_status();
+}
+
+template <typename T, int D, int BS>
+int dispatch_group(int G, const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                   int32_t num_heads, const int32_t* table, int32_t max_blocks,
+                   const int32_t* seqlens, int32_t max_parts, int32_t part_tokens, float scale,
+                   float* o_part, float* ml_part, hipStream_t stream) {
+#define PA_DECODE_G(GG)                                                                    \
+    case GG:                                                                               \
+        return launch_decode<T, D, BS, GG>(pool, out, q, batch, num_heads, table, max_blocks, \
+                                           seqlens, max_parts, part_tokens, scale, o_part,   \
+                                           ml_part, stream);
+    switch (G) {
+        PA_DECODE_G(1)
+        PA_DECODE_G(2)
+        PA_DECODE_G(4)
+        PA_DECODE_G(8)
+        default: return PA_ERR_UNSUPPORTED;
+    }
+#undef PA_DECODE_G
+}
+
+template <typename T>
+int dispatch_shape(int G, const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                   int32_t num_heads, const int32_t* table, int32_t max_blocks,
+                   const int32_t* seqlens, int32_t max_parts, int32_t part_tokens, float scale,
+                   float* o_part, float* ml_part, hipStream_t stream) {
+    const int D = pool->head_dim, BS = pool->block_size;
+#define PA_DECODE_SHAPE(DD, BB)                                                             \
+    if (D == DD && BS == BB)                                                                \
+        return dispatch_group<T, DD, BB>(G, pool, out, q, batch, num_heads, table, max_blocks, \
+                                         seqlens, max_parts, part_tokens, scale, o_part,      \
+                                         ml_part, stream);
+    PA_DECODE_SHAPE(64, 16)
+    PA_DECODE_SHAPE(64, 32)
+    PA_DECODE_SHAPE(128, 16)
+    PA_DECODE_SHAPE(128, 32)
+#undef PA_DECODE_SHAPE
+    return PA_ERR_UNSUPPORTED;
+}
+
+inline size_t workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
+                              int32_t max_parts) {
+    if (max_parts <= 1) return 0;
+    return static_cast<size_t>(batch) * num_heads * max_parts * (head_dim + 2) * sizeof(float);
+}
+
+inline int32_t num_parts(int32_t max_seqlen_k, int32_t part_tokens) {
+    return max_seqlen_k <= 0 ? 1 : (max_seqlen_k + part_tokens - 1) / part_tokens;
+}
+
+}  // namespace pa
+
+extern "C" size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
+                                            int32_t max_seqlen_k, int32_t partition_tokens,
+                                            int32_t block_size) {
+    using namespace pa;
+    if (batch <= 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0) return 0;
+    const int32_t p = pick_partition(partition_tokens, block_size);
+    return workspace_bytes(batch, num_heads, head_dim, num_parts(max_seqlen_k, p));
+}
+
+extern "C" int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                         int32_t num_heads, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* seqlens_k,
+                         int32_t max_seqlen_k, float softmax_scale, int32_t partition_tokens,
+                         void* workspace, size_t workspace_size, void* stream) {
+    using namespace pa;
+    int st = check_pool(pool);
+    if (st != PA_OK) return st;
+    if (batch < 0 || num_heads <= 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0 ||
+        partition_tokens < 0)
+        return PA_ERR_INVALID_ARG;
+    if (batch == 0) return PA_OK;
+    if (out == nullptr || q == nullptr || seqlens_k == nullptr ||
+        (max_blocks_per_seq > 0 && block_table == nullptr))
+        return PA_ERR_INVALID_ARG;
+    if (num_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (pool->num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
+    if (partition_tokens % pool->block_size != 0) return PA_ERR_INVALID_ARG;
+    if (batch > 65535) return PA_ERR_UNSUPPORTED;
+    const int32_t part_tokens = pick_partition(partition_tokens, pool->block_size);
+    if (part_tokens % pool->block_size != 0) return PA_ERR_INVALID_ARG;
+    // keys beyond the table width are never read, so the width also bounds the grid
+    const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * pool->block_size;
+    const int32_t eff_max = static_cast<int32_t>(std::min<int64_t>(max_seqlen_k, cap));
+    const int32_t max_parts = num_parts(eff_max, part_tokens);
+    const size_t need = workspace_bytes(batch, num_heads, pool->head_dim, max_parts);
+    if (need > 0 && (workspace == nullptr || workspace_size < need)) return PA_ERR_WORKSPACE;
+    float* o_part = static_cast<float*>(workspace);
+    float* ml_part = need ? o_part + static_cast<size_t>(batch) * num_heads * max_parts * pool->head_dim
+                          : nullptr;
+    const int G = num_heads / pool->num_kv_heads;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pool->dtype == PA_BF16)
+        return dispatch_shape<bf16_t>(G, pool, out, q, batch, num_heads, block_table,
+                                      max_blocks_per_seq, seqlens_k, max_parts, part_tokens,
+                                      softmax_scale, o_part, ml_part, s);
+    return dispatch_shape<float>(G, pool, out, q, batch, num_heads, block_table,
+                                 max_blocks_per_seq, seqlens_k, max_parts, part_tokens,
+                                 softmax_scale, o_part, ml_part, s);
+}

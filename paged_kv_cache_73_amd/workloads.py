@@ -216,3 +216,76 @@ def chunked_prefill(seed: int = 0, batch: int = 16, q_hi: int = 512, c_hi: int =
     new = [rng.randint(1, q_hi) for _ in range(batch)]
     cached = [rng.randint(0, c_hi) for _ in range(batch)]
     return prefill_workload(cached, new, seed=seed, name="chunked_prefill_r16")
+
+
+# --------------------------------------------------------------------------------------
+# driving a block manager through a workload
+# --------------------------------------------------------------------------------------
+
+@dataclass
+class Plan:
+    """Host metadata of a workload, produced by one block manager and its builders."""
+
+    tables: list[list[int]]       # [batch][max_blocks], -1 = unassigned
+    ctx_slots: list[int]          # slot of every k_ctx / v_ctx row
+    copies: list[tuple[int, int]] # copy-on-write pairs of the step, in order
+    new_slots: list[int]          # slot of every k_new / v_new row
+    seqlens_k: list[int]
+    cu_q: list[int]
+    cu_k: list[int]
+    max_q: int
+    max_k: int
+    manager: object = None
+
+
+def plan(w: Workload, manager_cls, slot_mapping, cu_seqlens) -> Plan:
+    """Replay the workload's block-manager calls on ``manager_cls`` and build the
+    metadata with the given builders.  The same sequence of calls is made whichever
+    implementation is passed (the library's or the oracle's); only they compute.
+
+    Context: every sequence's cached tokens get blocks (shared-prefix workloads take the
+    group's prefix blocks once, then share them with every member and release the
+    founding row).  Step: the new tokens' positions are made writable, which allocates
+    a block when a sequence crosses a block boundary and copies a shared block first.
+    """
+    B = w.block_size
+    bm = manager_cls(w.num_blocks, initial_order=w.order)
+    rows = [[-1] * w.max_blocks for _ in range(w.batch)]
+    ctx_seq, ctx_pos = [], []
+    if w.groups is None:
+        for b in range(w.batch):
+            bm.prepare_write(rows[b], 0, w.cached[b], B)
+            ctx_seq += [b] * w.cached[b]
+            ctx_pos += list(range(w.cached[b]))
+    else:
+        for members in w.groups:
+            base = [-1] * w.max_blocks
+            bm.prepare_write(base, 0, w.prefix_len, B)
+            for b in members:
+                rows[b] = bm.share(base)
+            bm.release_table(base)
+            ctx_seq += [members[0]] * w.prefix_len
+            ctx_pos += list(range(w.prefix_len))
+        for members in w.groups:
+            for b in members:
+                bm.prepare_write(rows[b], w.prefix_len, w.cached[b] - w.prefix_len, B)
+                ctx_seq += [b] * (w.cached[b] - w.prefix_len)
+                ctx_pos += list(range(w.prefix_len, w.cached[b]))
+        if w.snapshot_last:
+            for b in range(w.batch):
+                bm.incref(rows[b][(w.cached[b] - 1) // B])
+    ctx_slots = [int(x) for x in slot_mapping(rows, B, ctx_seq, ctx_pos)] if ctx_seq else []
+    copies = []
+    new_seq, new_pos = [], []
+    for b in range(w.batch):
+        copies += bm.prepare_write(rows[b], w.cached[b], w.new[b], B)
+        new_seq += [b] * w.new[b]
+        new_pos += list(range(w.cached[b], w.cached[b] + w.new[b]))
+    new_slots = [int(x) for x in slot_mapping(rows, B, new_seq, new_pos)] if new_seq else []
+    seqlens = w.seqlens_k
+    cu_q, max_q = cu_seqlens(w.new)
+    cu_k, max_k = cu_seqlens(seqlens)
+    return Plan(tables=[list(map(int, r)) for r in rows], ctx_slots=ctx_slots,
+                copies=[(int(s), int(d)) for s, d in copies], new_slots=new_slots,
+                seqlens_k=list(seqlens), cu_q=[int(x) for x in cu_q], cu_k=[int(x) for x in cu_k],
+                max_q=int(max_q), max_k=int(max_k), manager=bm)
