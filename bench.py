@@ -142,6 +142,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="decode launches timed after flushing the caches (reported apart)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -191,7 +193,7 @@ def main() -> int:
 
     # the same attention call after evicting L2 and the MALL by reading 1 GiB (a read
     # leaves clean lines, so the timed call pays no write-backs)
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     cold = []
     for _ in range(args.cold_reps):
         flush.sum()
@@ -201,7 +203,27 @@ def main() -> int:
         b.record(stream)
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b))
+    # attainable read bandwidth: plain streaming read of 2 GiB (best of a few grids)
+    import paged_kv_cache_73_amd as pa
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    attainable = 0.0
+    for grid in (4096, 8192):
+        pa.pa_probe_stream_read(flush, sink, grid)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            pa.pa_probe_stream_read(flush, sink, grid)
+        b.record(stream)
+        torch.cuda.synchronize()
+        attainable = max(attainable, 5 * flush.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9)
     del flush
+    if args.calibrate_copy:
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cold_median_ms = sorted(cold)[len(cold) // 2] if cold else None
 
     plan = r.plan
@@ -230,7 +252,9 @@ def main() -> int:
                 "algorithmic_bytes_per_launch": dbytes,
                 "launch_us_mean": attn_mean_ms * 1e3, "launch_us_median": attn_median_ms * 1e3,
                 "cold_launch_us_median": None if cold_median_ms is None else cold_median_ms * 1e3,
-                "cold_achieved": None if not cold_median_ms else dbytes / (cold_median_ms * 1e-3) / 1e9}
+                "cold_achieved": None if not cold_median_ms else dbytes / (cold_median_ms * 1e-3) / 1e9,
+                "attainable_stream_read": attainable,
+                "frac_of_attainable": achieved / attainable if attainable else None}
     else:
         fl = prefill_flops(w, plan)
         achieved = fl / (attn_mean_ms * 1e-3) / 1e12

@@ -156,6 +156,15 @@ int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t 
                       int32_t max_blocks_per_seq, float softmax_scale, int32_t causal,
                       void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * Measurement helper (not part of the attention path): reads `bytes` (a multiple of 16)
+ * of device memory at `buf` with non-temporal 16-byte loads from `grid` workgroups of
+ * 256 threads, as a plain streaming read; `sink` is a device word that is normally
+ * left untouched.  Timing it gives the attainable HBM read bandwidth that the decode
+ * kernel is compared with.
+ * ------------------------------------------------------------------------------- */
+int pa_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream);
+
 /* =================================================================================
  * Host-side block manager and metadata builders (no device memory, single-threaded;
  * every pointer below is host memory).

@@ -27,7 +27,7 @@ EXPORTS = [
     "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_free_stack",
     "pa_bm_alloc", "pa_bm_incref", "pa_bm_decref", "pa_bm_release_table", "pa_bm_share",
     "pa_bm_prepare_write", "pa_build_slot_mapping", "pa_build_cu_seqlens", "pa_pool_bytes",
-    "pa_validate_decode", "pa_validate_varlen", "pa_validate_slots",
+    "pa_validate_decode", "pa_validate_varlen", "pa_validate_slots", "pa_probe_stream_read",
 ]
 
 
@@ -104,6 +104,7 @@ def lib() -> ctypes.CDLL:
         "pa_validate_varlen": (ctypes.c_int, [_I32P, _I32, _I32, _I32P, _I32P, _I32, _I32, _I32,
                                               _I32, _I32P]),
         "pa_validate_slots": (ctypes.c_int, [_I32P, _I32, _I32, _I32, _I32P]),
+        "pa_probe_stream_read": (ctypes.c_int, [_VP, ctypes.c_size_t, _VP, _I32, _VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -142,6 +143,13 @@ def _dev(t, what: str) -> int:
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     return t.data_ptr()
+
+
+def _meta(t, what: str) -> int:
+    """Device int32 metadata (tables, lengths, offsets, slots, block ids)."""
+    if t is not None and str(t.dtype) != "torch.int32":
+        raise ValueError(f"{what} must be int32, got {t.dtype}")
+    return _dev(t, what)
 
 
 def _stream(stream) -> int:
@@ -187,14 +195,14 @@ def pa_abi_version() -> int:
 def pa_write_kv(pool: KVPool, k_new, v_new, slot_mapping, stream=None) -> None:
     n = int(slot_mapping.shape[0])
     st = lib().pa_write_kv(ctypes.byref(pool.struct), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
-                           _dev(slot_mapping, "slot_mapping"), n, _stream(stream))
+                           _meta(slot_mapping, "slot_mapping"), n, _stream(stream))
     if st:
         _raise(st, "pa_write_kv")
 
 
 def pa_copy_blocks(pool: KVPool, src, dst, stream=None) -> None:
     n = int(src.shape[0])
-    st = lib().pa_copy_blocks(ctypes.byref(pool.struct), _dev(src, "src"), _dev(dst, "dst"), n,
+    st = lib().pa_copy_blocks(ctypes.byref(pool.struct), _meta(src, "src"), _meta(dst, "dst"), n,
                               _stream(stream))
     if st:
         _raise(st, "pa_copy_blocks")
@@ -212,8 +220,8 @@ def pa_decode(pool: KVPool, out, q, block_table, seqlens_k, max_seqlen_k: int,
     batch, hq = int(q.shape[0]), int(q.shape[1])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().pa_decode(ctypes.byref(pool.struct), _dev(out, "out"), _dev(q, "q"), batch, hq,
-                         _dev(block_table, "block_table"), int(block_table.shape[1]),
-                         _dev(seqlens_k, "seqlens_k"), int(max_seqlen_k), float(softmax_scale),
+                         _meta(block_table, "block_table"), int(block_table.shape[1]),
+                         _meta(seqlens_k, "seqlens_k"), int(max_seqlen_k), float(softmax_scale),
                          int(partition_tokens), _dev(workspace, "workspace"), ws_bytes,
                          _stream(stream))
     if st:
@@ -225,13 +233,20 @@ def pa_prefill_varlen(pool: KVPool, out, q, cu_seqlens_q, cu_seqlens_k, max_seql
                       stream=None) -> None:
     batch = int(cu_seqlens_q.shape[0]) - 1
     st = lib().pa_prefill_varlen(ctypes.byref(pool.struct), _dev(out, "out"), _dev(q, "q"), batch,
-                                 int(q.shape[1]), _dev(cu_seqlens_q, "cu_seqlens_q"),
-                                 _dev(cu_seqlens_k, "cu_seqlens_k"), int(max_seqlen_q),
-                                 int(max_seqlen_k), _dev(block_table, "block_table"),
+                                 int(q.shape[1]), _meta(cu_seqlens_q, "cu_seqlens_q"),
+                                 _meta(cu_seqlens_k, "cu_seqlens_k"), int(max_seqlen_q),
+                                 int(max_seqlen_k), _meta(block_table, "block_table"),
                                  int(block_table.shape[1]), float(softmax_scale), int(bool(causal)),
                                  _stream(stream))
     if st:
         _raise(st, "pa_prefill_varlen")
+
+
+def pa_probe_stream_read(buf, sink, grid: int, stream=None) -> None:
+    st = lib().pa_probe_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                    _dev(sink, "sink"), int(grid), _stream(stream))
+    if st:
+        _raise(st, "pa_probe_stream_read")
 
 
 # --------------------------------------------------------------------------------------

@@ -34,7 +34,30 @@
 
 #include "common.h"
 
+// Tuning knobs (compile time).  Heads per workgroup: how many KV heads (one wave each)
+// share a workgroup; fewer means more, smaller workgroups and a shorter tail.
+#ifndef PA_DECODE_HPW
+#define PA_DECODE_HPW 2
+#endif
+// Occupancy hint: minimum waves per SIMD the register allocator must allow (0 = none).
+#ifndef PA_DECODE_WAVES_PER_EU
+#define PA_DECODE_WAVES_PER_EU 0
+#endif
+// Non-temporal K/V loads (the pages are streamed once).
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1
+#endif
+
 namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw buffer descriptor on CDNA (32-bit data format, no swizzle).
+constexpr int32_t kBufferDword3 = 0x00020000;
+// Cache policy of the K/V page loads: non-temporal (the pages are streamed once).
+constexpr int32_t kLoadPolicy = PA_DECODE_NT ? 2 : 0;
+
+__device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
 template <typename T, int D, int BS>
 struct PageShape {
@@ -47,34 +70,6 @@ struct PageShape {
     static_assert(kLanesPerRow >= 1 && kLanesPerRow <= kWave, "row size");
     static_assert(BS % kRowsPerLoad == 0, "block size vs rows per load");
 };
-
-// Online-softmax update of one lane's state with NS new base-2 scores.
-template <int NS, int E>
-__device__ __forceinline__ void fold(float& m, float& l, float (&o)[E], const float (&s)[NS],
-                                     const float (&v)[NS][E]) {
-    float mx = s[0];
-#pragma unroll
-    for (int i = 1; i < NS; ++i) mx = fmaxf(mx, s[i]);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing seen yet
-    const float corr = __builtin_amdgcn_exp2f(m - m_use);
-    float p[NS];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-        psum += p[i];
-    }
-    l = l * corr + psum;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        float acc = o[e] * corr;
-#pragma unroll
-        for (int i = 0; i < NS; ++i) acc += p[i] * v[i][e];
-        o[e] = acc;
-    }
-    m = m_new;
-}
 
 // Merge (m, l, o) with the state held by the lane `off` positions away (xor).
 template <int E>
@@ -94,8 +89,14 @@ __device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[E], int
     m = m_new;
 }
 
+#if PA_DECODE_WAVES_PER_EU > 0
+#define PA_DECODE_ATTR __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
+#else
+#define PA_DECODE_ATTR
+#endif
+
 template <typename T, int D, int BS, int G>
-__global__ __launch_bounds__(512) void decode_partial_kernel(
+__global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_partial_kernel(
     const T* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
     T* __restrict__ out, float* __restrict__ o_part, float* __restrict__ ml_part,
@@ -109,9 +110,9 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(
 
     const int lane = threadIdx.x % kWave;
     const int heads_per_wg = blockDim.x / kWave;
-    const int hkv = blockIdx.z * heads_per_wg + threadIdx.x / kWave;
-    const int b = blockIdx.y;
-    const int part = blockIdx.x;
+    const int hkv = blockIdx.x * heads_per_wg + threadIdx.x / kWave;
+    const int part = blockIdx.y;
+    const int b = blockIdx.z;
     const int r0 = lane / LPR;  // first row of this lane within a load
     const int c = lane % LPR;   // 16-byte piece of the row
 
@@ -145,16 +146,18 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(
         for (int e = 0; e < E; ++e) o[g][e] = 0.f;
     }
 
-    const int64_t page_bytes = static_cast<int64_t>(BS) * num_kv_heads * S::kRowBytes;
+    const int32_t page_bytes = BS * num_kv_heads * S::kRowBytes;
     // byte offset of this lane's first piece inside a page, and the step between loads
     const int32_t lane_off = (r0 * num_kv_heads + hkv) * S::kRowBytes + c * 16;
     const int32_t load_step = RPL * num_kv_heads * S::kRowBytes;
     const int32_t* table_row = block_table + static_cast<int64_t>(b) * max_blocks;
 
     // Consume one page of K/V already in registers.  A page whose block id is outside
-    // [0, num_blocks) was loaded from block 0 instead and is masked entirely.
+    // [0, num_blocks) was loaded from block 0 instead and is masked entirely.  Values are
+    // widened to fp32 one 16-byte piece at a time to keep few registers live.
     auto consume = [&](int32_t id, int32_t tok0, const uint4 (&kb)[NL], const uint4 (&vb)[NL]) {
         const bool valid = id >= 0 && id < num_blocks;
+        const bool partial = !valid || tok0 + BS > t_end;
         float s[G][NL];
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
@@ -168,35 +171,63 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(
                 s[g][j] = group_sum<LPR>(acc);
             }
         }
-        float vf[NL][E];
+        bool ok[NL];
 #pragma unroll
-        for (int j = 0; j < NL; ++j) widen(vb[j], vf[j], T{});
-        if (!valid || tok0 + BS > t_end) {
-            // last page of the sequence (or an unassigned block): select the rows to keep
+        for (int j = 0; j < NL; ++j) ok[j] = !partial || (valid && tok0 + r0 + j * RPL < t_end);
+        if (partial) {
+#pragma unroll
+            for (int j = 0; j < NL; ++j)
+#pragma unroll
+                for (int g = 0; g < G; ++g) s[g][j] = ok[j] ? s[g][j] : -INFINITY;
+        }
+        // online-softmax update of this lane's state with its NL rows
+        float p[G][NL];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float mx = s[g][0];
+#pragma unroll
+            for (int j = 1; j < NL; ++j) mx = fmaxf(mx, s[g][j]);
+            const float m_new = fmaxf(m[g], mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing seen yet
+            const float corr = __builtin_amdgcn_exp2f(m[g] - m_use);
+            float psum = 0.f;
 #pragma unroll
             for (int j = 0; j < NL; ++j) {
-                const bool ok = valid && tok0 + r0 + j * RPL < t_end;
-#pragma unroll
-                for (int g = 0; g < G; ++g) s[g][j] = ok ? s[g][j] : -INFINITY;
-#pragma unroll
-                for (int e = 0; e < E; ++e) vf[j][e] = ok ? vf[j][e] : 0.f;
+                p[g][j] = __builtin_amdgcn_exp2f(s[g][j] - m_use);
+                psum += p[g][j];
             }
+            l[g] = l[g] * corr + psum;
+            m[g] = m_new;
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[g][e] *= corr;
         }
 #pragma unroll
-        for (int g = 0; g < G; ++g) fold<NL, E>(m[g], l[g], o[g], s[g], vf);
+        for (int j = 0; j < NL; ++j) {
+            float vf[E];
+            widen(vb[j], vf, T{});
+            if (partial) {  // a masked row may hold anything (NaN): select, never multiply
+#pragma unroll
+                for (int e = 0; e < E; ++e) vf[e] = ok[j] ? vf[e] : 0.f;
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[g][e] += p[g][j] * vf[e];
+        }
     };
-    // Issue the loads of one page (always in bounds: invalid ids read block 0).
+    // Issue the loads of one page through a buffer descriptor spanning exactly that
+    // page: one 32-bit lane offset, the row step in the scalar offset, and accesses the
+    // hardware bounds-checks against the page.  Invalid ids read block 0 instead.
     auto load_page = [&](int32_t id, uint4 (&kd)[NL], uint4 (&vd)[NL]) {
-        const uint64_t base = static_cast<uint64_t>(static_cast<uint32_t>(
-                                  (id >= 0 && id < num_blocks) ? id : 0)) * page_bytes;
-        const char* kp = k_cache + base;
-        const char* vp = v_cache + base;
+        const int64_t base = static_cast<int64_t>((id >= 0 && id < num_blocks) ? id : 0) * page_bytes;
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(k_cache + base), 0, static_cast<int32_t>(page_bytes), kBufferDword3);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(v_cache + base), 0, static_cast<int32_t>(page_bytes), kBufferDword3);
 #pragma unroll
-        for (int j = 0; j < NL; ++j)
-            kd[j] = *reinterpret_cast<const uint4*>(kp + static_cast<uint32_t>(lane_off + j * load_step));
+        for (int j = 0; j < NL; ++j) kd[j] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(kr, lane_off, j * load_step, kLoadPolicy));
 #pragma unroll
-        for (int j = 0; j < NL; ++j)
-            vd[j] = *reinterpret_cast<const uint4*>(vp + static_cast<uint32_t>(lane_off + j * load_step));
+        for (int j = 0; j < NL; ++j) vd[j] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(vr, lane_off, j * load_step, kLoadPolicy));
     };
 
     if (num_blocks <= 0) pg1 = pg0;  // nothing can be read
@@ -269,20 +300,53 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     if (n_parts == 1) return;  // finished by pass 1
     const int64_t bh = static_cast<int64_t>(b) * num_heads + h;
     const float2* ml = reinterpret_cast<const float2*>(ml_part) + bh * max_parts;
+    const float* op = o_part + bh * max_parts * D;
+
+    // global maximum: lane p looks at partitions p, p+64, ...
     float M = -INFINITY;
-    for (int p = 0; p < n_parts; ++p) M = fmaxf(M, ml[p].x);
+    for (int p = lane; p < n_parts; p += kWave) M = fmaxf(M, ml[p].x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+    // boxed merge with m_new = M for every partition at once
     float L = 0.f, O[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) O[k] = 0.f;
     if (M != -INFINITY) {
-        for (int p = 0; p < n_parts; ++p) {
-            const float2 st = ml[p];
-            const float w = __builtin_amdgcn_exp2f(st.x - M);
-            L += w * st.y;
-            const float* op = o_part + (bh * max_parts + p) * D;
+        for (int p0 = 0; p0 < n_parts; p0 += kWave) {
+            const int cnt = min(kWave, n_parts - p0);
+            float wl = 0.f, ll = 0.f;
+            if (lane < cnt) {
+                const float2 st = ml[p0 + lane];
+                wl = __builtin_amdgcn_exp2f(st.x - M);
+                ll = st.y;
+            }
+            L += wl * ll;
+            // four partitions per trip so that their loads are in flight together
+            int i = 0;
+            for (; i + 4 <= cnt; i += 4) {
+                float v[4][PER], wi[4];
 #pragma unroll
-            for (int k = 0; k < PER; ++k) O[k] += w * op[lane + k * kWave];
+                for (int u = 0; u < 4; ++u) {
+                    wi[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i + u));
+                    const float* src = op + static_cast<int64_t>(p0 + i + u) * D + lane;
+#pragma unroll
+                    for (int k = 0; k < PER; ++k) v[u][k] = src[k * kWave];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int k = 0; k < PER; ++k) O[k] += wi[u] * v[u][k];
+            }
+            for (; i < cnt; ++i) {
+                const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+                const float* src = op + static_cast<int64_t>(p0 + i) * D + lane;
+#pragma unroll
+                for (int k = 0; k < PER; ++k) O[k] += wi * src[k * kWave];
+            }
         }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
@@ -310,9 +374,9 @@ int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batc
                   const int32_t* seqlens, int32_t max_parts, int32_t part_tokens, float scale,
                   float* o_part, float* ml_part, hipStream_t stream) {
     const int hkv = pool->num_kv_heads;
-    int per_wg = 8;
+    int per_wg = PA_DECODE_HPW;
     while (hkv % per_wg != 0) per_wg >>= 1;
-    const dim3 grid(max_parts, batch, hkv / per_wg);
+    const dim3 grid(hkv / per_wg, max_parts, batch);
     hipLaunchKernelGGL((decode_partial_kernel<T, D, BS, G>), grid, dim3(per_wg * kWave), 0, stream,
                        static_cast<const T*>(q), static_cast<const char*>(pool->k_cache),
                        static_cast<const char*>(pool->v_cache), table, seqlens,
@@ -412,6 +476,7 @@ extern "C" int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32
     const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * pool->block_size;
     const int32_t eff_max = static_cast<int32_t>(std::min<int64_t>(max_seqlen_k, cap));
     const int32_t max_parts = num_parts(eff_max, part_tokens);
+    if (max_parts > 65535) return PA_ERR_UNSUPPORTED;  // grid.y limit
     const size_t need = workspace_bytes(batch, num_heads, pool->head_dim, max_parts);
     if (need > 0 && (workspace == nullptr || workspace_size < need)) return PA_ERR_WORKSPACE;
     float* o_part = static_cast<float*>(workspace);

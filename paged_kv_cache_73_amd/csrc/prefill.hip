@@ -1,5 +1,274 @@
-// Varlen paged prefill (MFMA); filled in by the prefill kernel.
+// Varlen (packed) paged prefill on the matrix cores.
+//
+// What it computes ("从零开始写Qwen3（六）PagedAttention", fast-attn 库的使用: the varlen call
+// with a block table; "Sayfalı dikkat", Değişken uzunluklu yol): request i owns query
+// rows [cu_q[i], cu_q[i+1]) of the packed q and k_len = cu_k[i+1] - cu_k[i] keys, read
+// through block_table row i ("Paged attention 与 online softmax" §11.1).  With
+// c = k_len - q_len cached tokens, query row t sees keys j <= c + t when causal.
+//
+// How (gfx950, bf16 in, fp32 accumulate):
+// * One workgroup = 4 waves = 128 "rows" of one request and one KV head, a row being a
+//   (token, query head) pair: the G query heads sharing the KV head are packed next to
+//   each other, so every K/V tile read serves all of them.
+// * The keys are walked in tiles of 64 (a whole number of pages), FlashAttention-style
+//   ("结合nanovllm的FlashAttention和PagedAttention主要原理概述" 题目3): each tile is
+//   gathered page by page through the block table into LDS, scores are formed, folded
+//   into the running (m, l, O) with the §11.2 rule, and O is normalised once at the end.
+// * Transposed products keep every query row inside one lane: S^T = K Q^T with
+//   v_mfma_f32_32x32x16_bf16 (A = a K tile row per lane, B = the lane's q row), so lane
+//   l holds 16 scores of query row l%32 (the other 16 of the 32-key block sit in lane
+//   l^32).  The softmax is therefore lane-local apart from one exchange for the row max.
+//   O^T += V^T P^T then takes P straight from the S^T accumulators (the key order inside
+//   a 16-key step is permuted identically on both operands) and V^T from LDS.
+// * The next tile's K/V are loaded into registers while the current tile is computed.
+// * Masking selects: keys past the request, beyond the causal limit or in a block whose
+//   id is outside [0, num_blocks) are set to -inf before the exponent; their K/V are
+//   loaded as zeros (never from the pool), so no NaN can enter the products.
+
+#include <algorithm>
+
 #include "common.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kPrefillRows = 128;   // rows per workgroup (4 waves x 32)
+constexpr int kPrefillKeys = 64;    // keys per tile
+constexpr int kPrefillThreads = 256;
+
+template <int D, int G>
+__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
+    const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
+    const char* __restrict__ v_cache, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ block_table,
+    uint16_t* __restrict__ out, int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks,
+    int32_t block_size, int32_t max_blocks, float qscale, int32_t causal) {
+    constexpr int BN = kPrefillKeys;
+    constexpr int TOK = kPrefillRows / G;       // tokens per workgroup
+    constexpr int KS = D / 16;                  // MFMA k-steps over the head dim
+    constexpr int DB = D / 32;                  // 32-wide blocks of the head dim in O^T
+    constexpr int PITCH = D + 8;                // LDS row pitch (elements); the pad spreads banks
+    constexpr int CHUNKS = D / 8;               // 16-byte pieces per K/V row
+    constexpr int PIECES = BN * CHUNKS;         // pieces per tile (per K or V)
+    constexpr int PER_THREAD = PIECES / kPrefillThreads;
+    static_assert(PIECES % kPrefillThreads == 0, "tile split");
+
+    __shared__ __align__(16) uint16_t k_lds[BN * PITCH];
+    __shared__ __align__(16) uint16_t v_lds[BN * PITCH];
+    __shared__ uint8_t key_ok[BN];
+
+    const int req = blockIdx.z;
+    const int hkv = blockIdx.y;
+    const int q0 = cu_q[req];
+    const int q_len = cu_q[req + 1] - q0;
+    const int tok0 = blockIdx.x * TOK;
+    if (tok0 >= q_len) return;  // uniform: tile past this request's queries
+    const int k_len_req = cu_k[req + 1] - cu_k[req];
+    const int cached = k_len_req - q_len;                       // may be negative
+    const int k_len = min(k_len_req, max_blocks * block_size);  // keys past the table: never read
+    const int tok_last = min(tok0 + TOK, q_len) - 1;
+    const int kv_end = causal ? min(k_len, cached + tok_last + 1) : k_len;
+    const int n_tiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int w = tid / kWave;
+    const int h = lane / 32;      // which 8-wide half of a 16-wide k-step this lane feeds
+    const int r = lane % 32;
+    const int row = w * 32 + r;   // row of the workgroup this lane owns
+    const int tok = tok0 + row / G;
+    const int head = hkv * G + row % G;
+    const bool row_ok = tok < q_len;
+    const int row_limit = causal ? cached + tok : k_len - 1;    // last visible key
+    const int wave_first = min(tok0 + (w * 32) / G, q_len - 1);
+    const int wave_last = min(tok0 + (w * 32 + 31) / G, q_len - 1);
+    const int wave_lo = causal ? cached + wave_first : k_len - 1;  // all rows see keys <= this
+    const int wave_hi = causal ? cached + wave_last : k_len - 1;   // no row sees keys > this
+
+    // q row of this lane, pieces 16s + 8h .. +8 of the head dim
+    bf16x8_t qf[KS];
+    {
+        const uint16_t* qrow = q + (static_cast<int64_t>(q0 + tok) * num_heads + head) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (row_ok) u = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * h);
+            qf[s] = __builtin_bit_cast(bf16x8_t, u);
+        }
+    }
+
+    f32x16_t acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[db][x] = 0.f;
+    float m = -INFINITY, l = 0.f;
+
+    const int32_t* table_row = block_table + static_cast<int64_t>(req) * max_blocks;
+    const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * D * 2;  // bytes per slot
+
+    // global -> registers for one tile; zero for keys that must not be read
+    uint4 kr[PER_THREAD], vr[PER_THREAD];
+    bool okr[PER_THREAD];
+    auto fetch = [&](int t) {
+        const int j0 = t * BN;
+#pragma unroll
+        for (int u = 0; u < PER_THREAD; ++u) {
+            const int p = tid + u * kPrefillThreads;
+            const int key = p / CHUNKS;
+            const int chunk = p % CHUNKS;
+            const int j = j0 + key;
+            kr[u] = make_uint4(0, 0, 0, 0);
+            vr[u] = make_uint4(0, 0, 0, 0);
+            okr[u] = false;
+            if (j < kv_end) {
+                const int32_t id = table_row[j / block_size];
+                if (id >= 0 && id < num_blocks) {
+                    const int64_t off = (static_cast<int64_t>(id) * block_size + j % block_size) * row_stride +
+                                        static_cast<int64_t>(hkv) * D * 2 + chunk * 16;
+                    kr[u] = *reinterpret_cast<const uint4*>(k_cache + off);
+                    vr[u] = *reinterpret_cast<const uint4*>(v_cache + off);
+                    okr[u] = true;
+                }
+            }
+        }
+    };
+
+    if (n_tiles > 0) fetch(0);
+    for (int t = 0; t < n_tiles; ++t) {
+        const int j0 = t * BN;
+        __syncthreads();  // the previous tile is no longer read
+        bool my_ok = true;
+#pragma unroll
+        for (int u = 0; u < PER_THREAD; ++u) {
+            const int p = tid + u * kPrefillThreads;
+            const int key = p / CHUNKS;
+            const int chunk = p % CHUNKS;
+            *reinterpret_cast<uint4*>(&k_lds[key * PITCH + chunk * 8]) = kr[u];
+            *reinterpret_cast<uint4*>(&v_lds[key * PITCH + chunk * 8]) = vr[u];
+            if (chunk == 0) key_ok[key] = okr[u];
+            my_ok = my_ok && okr[u];
+        }
+        const bool tile_ok = __syncthreads_and(my_ok);
+        if (t + 1 < n_tiles) fetch(t + 1);  // in flight while this tile is computed
+
+        if (j0 > wave_hi) continue;  // no row of this wave sees any key of the tile
+
+        // S^T blocks: keys j0 + 32kb + (8i + 4h + jj), query row = this lane's row
+        f32x16_t s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int x = 0; x < 16; ++x) s[kb][x] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u16x8_t a = *reinterpret_cast<const u16x8_t*>(&k_lds[(kb * 32 + r) * PITCH + ks * 16 + 8 * h]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qf[ks], s[kb], 0, 0, 0);
+            }
+        }
+
+        // scale to base 2, mask, running max
+        const bool need_mask = !tile_ok || j0 + BN - 1 > wave_lo;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                float v = s[kb][x] * qscale;
+                if (need_mask) {
+                    const int key = kb * 32 + 8 * (x / 4) + 4 * h + (x % 4);
+                    const bool ok = key_ok[key] && j0 + key <= row_limit;
+                    v = ok ? v : -INFINITY;
+                }
+                s[kb][x] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float corr = __builtin_amdgcn_exp2f(m - m_use);
+        float psum = 0.f;
+        bf16x8_t pb[4];  // P^T operand of k-step ks: accumulators x = 8(ks%2) .. +8 of block ks/2
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(s[ks / 2][8 * (ks % 2) + e] - m_use);
+                psum += p;
+                pb[ks][e] = static_cast<__bf16>(p);
+            }
+        }
+        l = l * corr + psum;
+        m = m_new;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) acc[db][x] *= corr;
+
+        // O^T += V^T P^T: A = V^T rows d = 32db + r, keys 16ks + 4h + (e%4) + 8(e/4)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                u16x8_t a;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    a[e] = v_lds[(16 * ks + 4 * h + (e % 4) + 8 * (e / 4)) * PITCH + 32 * db + r];
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[ks], acc[db], 0, 0, 0);
+            }
+        }
+    }
+
+    // normalise and store: lane holds d = 32db + 8i + 4h + jj of its row
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (!row_ok) return;
+    uint16_t* orow = out + (static_cast<int64_t>(q0 + tok) * num_heads + head) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            uint32_t lo = static_cast<uint32_t>(to_bf16_bits(acc[db][4 * i4 + 0] * inv)) |
+                          (static_cast<uint32_t>(to_bf16_bits(acc[db][4 * i4 + 1] * inv)) << 16);
+            uint32_t hi = static_cast<uint32_t>(to_bf16_bits(acc[db][4 * i4 + 2] * inv)) |
+                          (static_cast<uint32_t>(to_bf16_bits(acc[db][4 * i4 + 3] * inv)) << 16);
+            *reinterpret_cast<uint2*>(orow + 32 * db + 8 * i4 + 4 * h) = make_uint2(lo, hi);
+        }
+}
+
+template <int D, int G>
+int launch_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                   int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
+                   int32_t max_seqlen_q, const int32_t* table, int32_t max_blocks,
+                   float scale, int32_t causal, hipStream_t stream) {
+    const int tok_per_wg = kPrefillRows / G;
+    const dim3 grid((max_seqlen_q + tok_per_wg - 1) / tok_per_wg, pool->num_kv_heads, batch);
+    hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kPrefillThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const char*>(pool->k_cache),
+                       static_cast<const char*>(pool->v_cache), cu_q, cu_k, table,
+                       static_cast<uint16_t*>(out), num_heads, pool->num_kv_heads,
+                       pool->num_blocks, pool->block_size, max_blocks, scale * kLog2e, causal);
+    return launch_status();
+}
+
+template <int D>
+int dispatch_prefill_group(int G, const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                           int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
+                           int32_t max_seqlen_q, const int32_t* table, int32_t max_blocks,
+                           float scale, int32_t causal, hipStream_t stream) {
+    switch (G) {
+        case 1: return launch_prefill<D, 1>(pool, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, table, max_blocks, scale, causal, stream);
+        case 2: return launch_prefill<D, 2>(pool, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, table, max_blocks, scale, causal, stream);
+        case 4: return launch_prefill<D, 4>(pool, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, table, max_blocks, scale, causal, stream);
+        case 8: return launch_prefill<D, 8>(pool, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, table, max_blocks, scale, causal, stream);
+        default: return PA_ERR_UNSUPPORTED;
+    }
+}
+
+}  // namespace pa
 
 extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                                  int32_t num_heads, const int32_t* cu_seqlens_q,
@@ -7,8 +276,30 @@ extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* 
                                  int32_t max_seqlen_k, const int32_t* block_table,
                                  int32_t max_blocks_per_seq, float softmax_scale, int32_t causal,
                                  void* stream) {
-    (void)pool; (void)out; (void)q; (void)batch; (void)num_heads; (void)cu_seqlens_q;
-    (void)cu_seqlens_k; (void)max_seqlen_q; (void)max_seqlen_k; (void)block_table;
-    (void)max_blocks_per_seq; (void)softmax_scale; (void)causal; (void)stream;
+    using namespace pa;
+    int st = check_pool(pool);
+    if (st != PA_OK) return st;
+    if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
+        max_blocks_per_seq < 0)
+        return PA_ERR_INVALID_ARG;
+    if (batch == 0 || max_seqlen_q == 0) return PA_OK;
+    if (out == nullptr || q == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
+        (max_blocks_per_seq > 0 && block_table == nullptr))
+        return PA_ERR_INVALID_ARG;
+    if (num_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (pool->block_size != 16 && pool->block_size != 32) return PA_ERR_UNSUPPORTED;
+    if (batch > 65535 || pool->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+    (void)max_seqlen_k;  // the per-request lengths bound the key loop
+    const int G = num_heads / pool->num_kv_heads;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pool->head_dim == 128)
+        return dispatch_prefill_group<128>(G, pool, out, q, batch, num_heads, cu_seqlens_q,
+                                           cu_seqlens_k, max_seqlen_q, block_table,
+                                           max_blocks_per_seq, softmax_scale, causal != 0, s);
+    if (pool->head_dim == 64)
+        return dispatch_prefill_group<64>(G, pool, out, q, batch, num_heads, cu_seqlens_q,
+                                          cu_seqlens_k, max_seqlen_q, block_table,
+                                          max_blocks_per_seq, softmax_scale, causal != 0, s);
     return PA_ERR_UNSUPPORTED;
 }

@@ -1,0 +1,35 @@
+// Measurement helper: the attainable HBM read bandwidth of this GPU, for comparison with
+// the attention kernels.  Every lane streams 16-byte pieces of a large buffer with
+// non-temporal loads (the same load form as the decode pages) and folds them into a
+// value that is stored only if it matches an impossible pattern, so nothing but the
+// reads reaches memory.
+
+#include "common.h"
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, int64_t n,
+                                                          uint32_t* __restrict__ sink) {
+    uint32_t acc = 0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+#pragma unroll 8
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(p + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+}  // namespace pa
+
+extern "C" int pa_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid,
+                                    void* stream) {
+    using namespace pa;
+    if (buf == nullptr || sink == nullptr || grid <= 0 || bytes % 16 != 0) return PA_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(buf), static_cast<int64_t>(bytes / 16),
+                       static_cast<uint32_t*>(sink));
+    return launch_status();
+}
