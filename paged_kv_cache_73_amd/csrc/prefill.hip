@@ -38,14 +38,15 @@ typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kPrefillRows = 128;   // rows per workgroup (4 waves x 32)
 constexpr int kPrefillKeys = 64;    // keys per tile
 constexpr int kPrefillThreads = 256;
+constexpr int kXcds = 8;            // accelerator complex dies of an MI355X
 
-template <int D, int G>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
+template <int D, int G, int BS>
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, const int32_t* __restrict__ block_table,
     uint16_t* __restrict__ out, int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks,
-    int32_t block_size, int32_t max_blocks, float qscale, int32_t causal) {
+    int32_t max_blocks, float qscale, int32_t causal, int32_t n_qtiles, int32_t n_groups) {
     constexpr int BN = kPrefillKeys;
     constexpr int TOK = kPrefillRows / G;       // tokens per workgroup
     constexpr int KS = D / 16;                  // MFMA k-steps over the head dim
@@ -60,18 +61,27 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
     __shared__ __align__(16) uint16_t v_lds[BN * PITCH];
     __shared__ uint8_t key_ok[BN];
 
-    const int req = blockIdx.z;
-    const int hkv = blockIdx.y;
+    // Workgroups are handed to the 8 XCDs round-robin (id L runs on XCD L % 8).  All
+    // query tiles of one (request, KV head) group read the same K/V pages, so they are
+    // kept on one XCD (sharing its L2): group g runs on XCD g % 8, and each XCD walks its
+    // groups in order, the query tiles of a group back to back.
+    const int L = blockIdx.x;
+    const int slot = L / kXcds;
+    const int group = (slot / n_qtiles) * kXcds + L % kXcds;
+    if (group >= n_groups) return;  // grid padding
+    const int hkv = group % num_kv_heads;
+    const int req = group / num_kv_heads;
     const int q0 = cu_q[req];
     const int q_len = cu_q[req + 1] - q0;
-    const int tok0 = blockIdx.x * TOK;
+    // later query tiles see more keys under the causal mask: start them first
+    const int tok0 = (n_qtiles - 1 - slot % n_qtiles) * TOK;
     if (tok0 >= q_len) return;  // uniform: tile past this request's queries
     const int k_len_req = cu_k[req + 1] - cu_k[req];
     const int cached = k_len_req - q_len;                       // may be negative
-    const int k_len = min(k_len_req, max_blocks * block_size);  // keys past the table: never read
+    const int k_len = min(k_len_req, max_blocks * BS);  // keys past the table: never read
     const int tok_last = min(tok0 + TOK, q_len) - 1;
     const int kv_end = causal ? min(k_len, cached + tok_last + 1) : k_len;
-    const int n_tiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+    const int n_tiles = (kv_end > 0 && num_blocks > 0) ? (kv_end + BN - 1) / BN : 0;
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -82,11 +92,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
     const int tok = tok0 + row / G;
     const int head = hkv * G + row % G;
     const bool row_ok = tok < q_len;
-    const int row_limit = causal ? cached + tok : k_len - 1;    // last visible key
+    // last key each row may see (the causal limit and the request's end)
+    const int row_limit = min(causal ? cached + tok : k_len - 1, kv_end - 1);
     const int wave_first = min(tok0 + (w * 32) / G, q_len - 1);
     const int wave_last = min(tok0 + (w * 32 + 31) / G, q_len - 1);
-    const int wave_lo = causal ? cached + wave_first : k_len - 1;  // all rows see keys <= this
-    const int wave_hi = causal ? cached + wave_last : k_len - 1;   // no row sees keys > this
+    const int wave_lo = min(causal ? cached + wave_first : k_len - 1, kv_end - 1);  // all rows see keys <= this
+    const int wave_hi = min(causal ? cached + wave_last : k_len - 1, kv_end - 1);   // no row sees keys > this
 
     // q row of this lane, pieces 16s + 8h .. +8 of the head dim
     bf16x8_t qf[KS];
@@ -110,34 +121,47 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
     const int32_t* table_row = block_table + static_cast<int64_t>(req) * max_blocks;
     const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * D * 2;  // bytes per slot
 
-    // global -> registers for one tile; zero for keys that must not be read
+    // Block ids of this thread's pieces are loaded one tile before the K/V they address,
+    // so a tile's loads never wait on a table lookup.
+    int32_t ids[PER_THREAD];
+    auto fetch_ids = [&](int t) {
+        const int j0 = t * BN;
+#pragma unroll
+        for (int u = 0; u < PER_THREAD; ++u) {
+            const int j = j0 + (tid + u * kPrefillThreads) / CHUNKS;
+            ids[u] = table_row[min(j, kv_end - 1) / BS];
+        }
+    };
+    // global -> registers for one tile, without branches: a piece that must not be read
+    // (past the end, or an id outside the pool) loads from the pool's first row and is
+    // replaced by zeros.
     uint4 kr[PER_THREAD], vr[PER_THREAD];
-    bool okr[PER_THREAD];
+    bool okr[PER_THREAD], ldr[PER_THREAD];
     auto fetch = [&](int t) {
         const int j0 = t * BN;
 #pragma unroll
         for (int u = 0; u < PER_THREAD; ++u) {
             const int p = tid + u * kPrefillThreads;
-            const int key = p / CHUNKS;
-            const int chunk = p % CHUNKS;
-            const int j = j0 + key;
-            kr[u] = make_uint4(0, 0, 0, 0);
-            vr[u] = make_uint4(0, 0, 0, 0);
-            okr[u] = false;
-            if (j < kv_end) {
-                const int32_t id = table_row[j / block_size];
-                if (id >= 0 && id < num_blocks) {
-                    const int64_t off = (static_cast<int64_t>(id) * block_size + j % block_size) * row_stride +
-                                        static_cast<int64_t>(hkv) * D * 2 + chunk * 16;
-                    kr[u] = *reinterpret_cast<const uint4*>(k_cache + off);
-                    vr[u] = *reinterpret_cast<const uint4*>(v_cache + off);
-                    okr[u] = true;
-                }
-            }
+            const int j = j0 + p / CHUNKS;
+            const int32_t id = ids[u];
+            const bool ok = j < kv_end && static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks);
+            const int64_t off = ok ? (static_cast<int64_t>(id) * BS + j % BS) * row_stride +
+                                         static_cast<int64_t>(hkv) * D * 2 + (p % CHUNKS) * 16
+                                   : 0;
+            // consumed (and zeroed when !ok) only when stored to LDS in the next iteration,
+            // so the loads stay in flight while the current tile is computed
+            kr[u] = *reinterpret_cast<const uint4*>(k_cache + off);
+            vr[u] = *reinterpret_cast<const uint4*>(v_cache + off);
+            ldr[u] = ok;
+            okr[u] = ok || j >= kv_end;  // false only for an unassigned block inside the range
         }
     };
 
-    if (n_tiles > 0) fetch(0);
+    if (n_tiles > 0) {
+        fetch_ids(0);
+        fetch(0);
+        if (n_tiles > 1) fetch_ids(1);
+    }
     for (int t = 0; t < n_tiles; ++t) {
         const int j0 = t * BN;
         __syncthreads();  // the previous tile is no longer read
@@ -147,13 +171,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
             const int p = tid + u * kPrefillThreads;
             const int key = p / CHUNKS;
             const int chunk = p % CHUNKS;
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            if (!ldr[u]) kr[u] = z, vr[u] = z;
             *reinterpret_cast<uint4*>(&k_lds[key * PITCH + chunk * 8]) = kr[u];
             *reinterpret_cast<uint4*>(&v_lds[key * PITCH + chunk * 8]) = vr[u];
             if (chunk == 0) key_ok[key] = okr[u];
             my_ok = my_ok && okr[u];
         }
         const bool tile_ok = __syncthreads_and(my_ok);
-        if (t + 1 < n_tiles) fetch(t + 1);  // in flight while this tile is computed
+        if (t + 1 < n_tiles) {  // in flight while this tile is computed
+            fetch(t + 1);
+            if (t + 2 < n_tiles) fetch_ids(t + 2);
+        }
 
         if (j0 > wave_hi) continue;  // no row of this wave sees any key of the tile
 
@@ -172,21 +201,34 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
 
         // scale to base 2, mask, running max
         const bool need_mask = !tile_ok || j0 + BN - 1 > wave_lo;
+        const int lim = row_limit - j0;  // keys of this tile with index <= lim are visible
+        // qscale > 0, so the max of the raw scores scales to the max of the scaled ones.
+        // Masking (wave-uniform branches): keys past a row's limit always; keys of an
+        // unassigned block only in the rare tile that has one.
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int key = kb * 32 + 8 * (x / 4) + 4 * h + (x % 4);
+                    s[kb][x] = key <= lim ? s[kb][x] : -INFINITY;
+                }
+            if (!tile_ok) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int x = 0; x < 16; ++x) {
+                        const int key = kb * 32 + 8 * (x / 4) + 4 * h + (x % 4);
+                        s[kb][x] = key_ok[key] ? s[kb][x] : -INFINITY;
+                    }
+            }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                float v = s[kb][x] * qscale;
-                if (need_mask) {
-                    const int key = kb * 32 + 8 * (x / 4) + 4 * h + (x % 4);
-                    const bool ok = key_ok[key] && j0 + key <= row_limit;
-                    v = ok ? v : -INFINITY;
-                }
-                s[kb][x] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[kb][x]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * qscale;
         const float m_new = fmaxf(m, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float corr = __builtin_amdgcn_exp2f(m - m_use);
@@ -196,17 +238,19 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(s[ks / 2][8 * (ks % 2) + e] - m_use);
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[ks / 2][8 * (ks % 2) + e], qscale, -m_use));
                 psum += p;
                 pb[ks][e] = static_cast<__bf16>(p);
             }
         }
         l = l * corr + psum;
         m = m_new;
+        if (__builtin_amdgcn_read_exec() & __ballot(corr != 1.f)) {  // some row's max moved
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) acc[db][x] *= corr;
+                for (int x = 0; x < 16; ++x) acc[db][x] *= corr;
+        }
 
         // O^T += V^T P^T: A = V^T rows d = 32db + r, keys 16ks + 4h + (e%4) + 8(e/4)
 #pragma unroll
@@ -239,18 +283,23 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
         }
 }
 
-template <int D, int G>
+template <int D, int G, int BS>
 int launch_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                    int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
                    int32_t max_seqlen_q, const int32_t* table, int32_t max_blocks,
                    float scale, int32_t causal, hipStream_t stream) {
     const int tok_per_wg = kPrefillRows / G;
-    const dim3 grid((max_seqlen_q + tok_per_wg - 1) / tok_per_wg, pool->num_kv_heads, batch);
-    hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kPrefillThreads), 0, stream,
+    const int64_t n_qtiles = (max_seqlen_q + tok_per_wg - 1) / tok_per_wg;
+    const int64_t n_groups = static_cast<int64_t>(pool->num_kv_heads) * batch;
+    const int64_t padded = (n_groups + kXcds - 1) / kXcds * n_qtiles * kXcds;
+    if (padded > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    const dim3 grid(static_cast<uint32_t>(padded));
+    hipLaunchKernelGGL((prefill_kernel<D, G, BS>), grid, dim3(kPrefillThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const char*>(pool->k_cache),
                        static_cast<const char*>(pool->v_cache), cu_q, cu_k, table,
                        static_cast<uint16_t*>(out), num_heads, pool->num_kv_heads,
-                       pool->num_blocks, pool->block_size, max_blocks, scale * kLog2e, causal);
+                       pool->num_blocks, max_blocks, scale * kLog2e, causal,
+                       static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups));
     return launch_status();
 }
 
@@ -259,13 +308,23 @@ int dispatch_prefill_group(int G, const pa_kv_pool* pool, void* out, const void*
                            int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
                            int32_t max_seqlen_q, const int32_t* table, int32_t max_blocks,
                            float scale, int32_t causal, hipStream_t stream) {
+#define PA_PREFILL_CASE(GG)                                                                     \
+    case GG:                                                                                    \
+        return pool->block_size == 16                                                          \
+                   ? launch_prefill<D, GG, 16>(pool, out, q, batch, num_heads, cu_q, cu_k,      \
+                                               max_seqlen_q, table, max_blocks, scale, causal,  \
+                                               stream)                                          \
+                   : launch_prefill<D, GG, 32>(pool, out, q, batch, num_heads, cu_q, cu_k,      \
+                                               max_seqlen_q, table, max_blocks, scale, causal,  \
+                                               stream);
     switch (G) {
-        case 1: return launch_prefill<D, 1>(pool, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, table, max_blocks, scale, causal, stream);
-        case 2: return launch_prefill<D, 2>(pool, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, table, max_blocks, scale, causal, stream);
-        case 4: return launch_prefill<D, 4>(pool, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, table, max_blocks, scale, causal, stream);
-        case 8: return launch_prefill<D, 8>(pool, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, table, max_blocks, scale, causal, stream);
+        PA_PREFILL_CASE(1)
+        PA_PREFILL_CASE(2)
+        PA_PREFILL_CASE(4)
+        PA_PREFILL_CASE(8)
         default: return PA_ERR_UNSUPPORTED;
     }
+#undef PA_PREFILL_CASE
 }
 
 }  // namespace pa
@@ -289,7 +348,7 @@ extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* 
     if (num_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
     if (pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
     if (pool->block_size != 16 && pool->block_size != 32) return PA_ERR_UNSUPPORTED;
-    if (batch > 65535 || pool->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;
     (void)max_seqlen_k;  // the per-request lengths bound the key loop
     const int G = num_heads / pool->num_kv_heads;
     const hipStream_t s = static_cast<hipStream_t>(stream);
