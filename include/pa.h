@@ -124,9 +124,9 @@ int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src, const int32_t* ds
  * workspace: device scratch of at least pa_decode_workspace_bytes(...) bytes (may be
  *   NULL when that is 0); its contents need no initialisation.
  * ------------------------------------------------------------------------------- */
-size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
-                                 int32_t max_seqlen_k, int32_t partition_tokens,
-                                 int32_t block_size);
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seqlen_k,
+                                 int32_t partition_tokens, int32_t block_size);
 
 int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
               int32_t num_heads, const int32_t* block_table, int32_t max_blocks_per_seq,

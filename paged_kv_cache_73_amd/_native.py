@@ -80,7 +80,7 @@ def lib() -> ctypes.CDLL:
         "pa_abi_version": (_I32, []),
         "pa_write_kv": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _VP, _I32, _VP]),
         "pa_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _VP]),
-        "pa_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 6),
+        "pa_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7),
         "pa_decode": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP, _I32, _VP,
                                      _I32, ctypes.c_float, _I32, _VP, ctypes.c_size_t, _VP]),
         "pa_prefill_varlen": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP, _VP,
@@ -208,10 +208,10 @@ def pa_copy_blocks(pool: KVPool, src, dst, stream=None) -> None:
         _raise(st, "pa_copy_blocks")
 
 
-def pa_decode_workspace_bytes(batch, num_heads, head_dim, max_seqlen_k, partition_tokens,
-                              block_size) -> int:
-    return int(lib().pa_decode_workspace_bytes(batch, num_heads, head_dim, max_seqlen_k,
-                                               partition_tokens, block_size))
+def pa_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_seqlen_k,
+                              partition_tokens, block_size) -> int:
+    return int(lib().pa_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim,
+                                               max_seqlen_k, partition_tokens, block_size))
 
 
 def pa_decode(pool: KVPool, out, q, block_table, seqlens_k, max_seqlen_k: int,

@@ -360,12 +360,23 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     }
 }
 
-constexpr int kDefaultPartitionTokens = 256;
+// Automatic split-K partition length.  A partition is one workgroup's share of a
+// sequence; the aim is about kTargetWorkgroups workgroups in total (seven per CU of the
+// 256 on an MI355X: enough to keep every CU fed, few enough that each streams a long
+// run of pages and the merge stays small), assuming contexts average 60 % of the
+// maximum.  Rounded to 64 tokens and kept within [128, 4096].
+constexpr int64_t kTargetWorkgroups = 7 * 256;
 
-inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size) {
-    int32_t p = partition_tokens > 0 ? partition_tokens : kDefaultPartitionTokens;
-    if (p < block_size) p = block_size;
-    return p;
+inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size, int32_t batch,
+                              int32_t num_kv_heads, int32_t max_seqlen_k) {
+    if (partition_tokens > 0) return partition_tokens < block_size ? block_size : partition_tokens;
+    int per_wg = PA_DECODE_HPW;
+    while (num_kv_heads % per_wg != 0) per_wg >>= 1;
+    const int64_t groups = num_kv_heads / per_wg;
+    const int64_t est_keys = static_cast<int64_t>(batch) * max_seqlen_k * 6 / 10;
+    int64_t p = (est_keys * groups / kTargetWorkgroups + 63) / 64 * 64;
+    p = std::max<int64_t>(128, std::min<int64_t>(4096, p));
+    return static_cast<int32_t>((p + block_size - 1) / block_size * block_size);
 }
 
 template <typename T, int D, int BS, int G>
@@ -442,12 +453,14 @@ inline int32_t num_parts(int32_t max_seqlen_k, int32_t part_tokens) {
 
 }  // namespace pa
 
-extern "C" size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
+extern "C" size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
                                             int32_t max_seqlen_k, int32_t partition_tokens,
                                             int32_t block_size) {
     using namespace pa;
-    if (batch <= 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0) return 0;
-    const int32_t p = pick_partition(partition_tokens, block_size);
+    if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+        return 0;
+    const int32_t p = pick_partition(partition_tokens, block_size, batch, num_kv_heads, max_seqlen_k);
     return workspace_bytes(batch, num_heads, head_dim, num_parts(max_seqlen_k, p));
 }
 
@@ -470,7 +483,8 @@ extern "C" int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32
     if (pool->num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
     if (partition_tokens % pool->block_size != 0) return PA_ERR_INVALID_ARG;
     if (batch > 65535) return PA_ERR_UNSUPPORTED;
-    const int32_t part_tokens = pick_partition(partition_tokens, pool->block_size);
+    const int32_t part_tokens = pick_partition(partition_tokens, pool->block_size, batch,
+                                               pool->num_kv_heads, max_seqlen_k);
     if (part_tokens % pool->block_size != 0) return PA_ERR_INVALID_ARG;
     // keys beyond the table width are never read, so the width also bounds the grid
     const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * pool->block_size;

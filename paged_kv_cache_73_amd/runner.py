@@ -63,8 +63,8 @@ def setup(w: W.Workload, dev="cuda") -> DeviceRun:
 
 def ensure_workspace(w: W.Workload, r: DeviceRun, partition_tokens: int) -> None:
     max_k = max(r.plan.seqlens_k) if r.plan.seqlens_k else 0
-    ws = pa.pa_decode_workspace_bytes(w.batch, w.num_heads, w.head_dim, max_k, partition_tokens,
-                                      w.block_size)
+    ws = pa.pa_decode_workspace_bytes(w.batch, w.num_heads, w.num_kv_heads, w.head_dim, max_k,
+                                      partition_tokens, w.block_size)
     if r.workspace is None or r.workspace.numel() < ws:
         r.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=r.q.device)
 

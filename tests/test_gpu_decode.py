@@ -184,7 +184,7 @@ def test_decode_unassigned_block_is_masked():
     table[1, 2] = 10 ** 6       # id beyond the pool: never read
     t = torch.tensor(table, dtype=torch.int32, device="cuda")
     pa.pa_decode(g.pool, g.out, g.q, t, g.seqlens, 41, w.scale, 16,
-                 torch.empty(pa.pa_decode_workspace_bytes(2, 4, 64, 41, 16, 16), dtype=torch.uint8,
+                 torch.zeros(pa.pa_decode_workspace_bytes(2, 4, 2, 64, 41, 16, 16), dtype=torch.uint8,
                              device="cuda"))
     torch.cuda.synchronize()
     from oracle import attention as OA
@@ -198,8 +198,8 @@ def test_decode_unassigned_block_is_masked():
 def test_decode_workspace_and_argument_errors():
     w = W.decode_workload([700, 20], dtype="bf16", seed=15)
     g = H.gpu_setup(w)
-    need = pa.pa_decode_workspace_bytes(2, 16, 128, 701, 64, 16)
-    assert need == 2 * 16 * 11 * 130 * 4
+    need = pa.pa_decode_workspace_bytes(2, 16, 8, 128, 701, 64, 16)
+    assert need == 2 * 16 * 11 * 130 * 4   # (o, m, l) per (sequence, head, partition)
     small = torch.empty(need - 4, dtype=torch.uint8, device="cuda")
     with pytest.raises(pa.PaError) as e:
         pa.pa_decode(g.pool, g.out, g.q, g.table, g.seqlens, 701, w.scale, 64, small)
@@ -226,6 +226,33 @@ def test_decode_qwen3_b64_full():
 def test_decode_long_context_split_k(partition_tokens):
     w = W.long_decode(seed=0)
     _check_decode(w, partition_tokens, rows=[0, 3, 7], what=f"long P={partition_tokens}")
+
+
+def test_decode_workspace_reuse_across_calls_and_shapes():
+    # the workspace holds nothing between calls: any earlier contents are overwritten
+    w = W.decode_workload([900, 40, 2100, 300], dtype="bf16", seed=16)
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g, 64)
+    torch.cuda.synchronize()
+    first = g.out.clone()
+    for p in (64, 128, 64, 256):
+        g.out.zero_()
+        H.gpu_step(w, g, p, attention=True)
+        torch.cuda.synchronize()
+        H.assert_close(H.out_f64(g.out), H.out_f64(first), "bf16", f"reuse P={p}")
+    ws = g.workspace
+    ws.fill_(0xFF)  # garbage (NaN patterns) must not matter
+    H.gpu_step(w, g, 64)
+    torch.cuda.synchronize()
+    H.assert_close(H.out_f64(g.out), H.out_f64(first), "bf16", "garbage workspace")
+    # a smaller problem on the same workspace
+    w2 = W.decode_workload([700, 33], dtype="bf16", seed=17)
+    g2 = H.gpu_setup(w2)
+    g2.workspace = ws
+    _, o2 = None, H.oracle_run(w2)
+    H.gpu_step(w2, g2, 64)
+    torch.cuda.synchronize()
+    H.assert_close(H.out_f64(g2.out), o2.out, "bf16", "smaller problem, reused workspace")
 
 
 def test_decode_shared_prefix_with_copy_on_write():

@@ -64,7 +64,7 @@ def test_prefill_single_query_equals_decode():
     g, o = _run(w)
     # the same inputs through pa_decode
     out = torch.empty_like(g.out)
-    ws = torch.empty(pa.pa_decode_workspace_bytes(5, 16, 128, 501, 0, 16), dtype=torch.uint8,
+    ws = torch.zeros(pa.pa_decode_workspace_bytes(5, 16, 8, 128, 501, 0, 16), dtype=torch.uint8,
                      device="cuda")
     pa.pa_decode(g.pool, out, g.q, g.table, g.seqlens, 501, w.scale, 0, ws)
     torch.cuda.synchronize()
