@@ -117,12 +117,18 @@ int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src, const int32_t* ds
  * seqlens_k: device int32 [batch], 0 <= seqlens_k[b] <= min(max_seqlen_k,
  *   max_blocks_per_seq*B).  Keys beyond max_blocks_per_seq*B are never read.
  * max_seqlen_k: host bound on seqlens_k, sizes the grid and the workspace.
- * partition_tokens: split-K partition length (a multiple of B; 0 picks a default).
+ * partition_tokens: split-K partition length (a multiple of B), or 0 for an automatic
+ *   choice from batch, num_kv_heads and max_seqlen_k (about seven workgroups per CU).
  *   Keys are cut into partitions processed by different workgroups; each yields an
  *   online-softmax state (m, l, o) and a second kernel merges them with the [PA11]
  *   §11.2 rule.  Sequences with one partition are finished by the first kernel.
- * workspace: device scratch of at least pa_decode_workspace_bytes(...) bytes (may be
- *   NULL when that is 0); its contents need no initialisation.
+ * workspace: device scratch of at least pa_decode_workspace_bytes(...) bytes, called with
+ *   the same batch, heads, head_dim, max_seqlen_k, partition_tokens and block size (may
+ *   be NULL when that is 0).  Its contents need no initialisation and are meaningless
+ *   after the call; calls that share a workspace must not overlap.
+ * Errors: PA_ERR_INVALID_ARG (null pointers, num_heads not a multiple of num_kv_heads,
+ *   partition_tokens not a multiple of B), PA_ERR_WORKSPACE, PA_ERR_UNSUPPORTED (shape,
+ *   batch > 65535).
  * ------------------------------------------------------------------------------- */
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_seqlen_k,
@@ -147,7 +153,11 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
  *   K/V must already be written).  With c = k_len - q_len cached tokens, query row t
  *   sees keys j <= c + t when causal != 0 (bottom-right alignment), all k_len keys
  *   otherwise.  A row that sees no key gets zeros.
- * max_seqlen_q, max_seqlen_k: host bounds on the per-request lengths (grid sizing).
+ * max_seqlen_q, max_seqlen_k: host bounds on the per-request lengths (grid sizing);
+ *   queries of a request beyond max_seqlen_q are not computed.
+ * softmax_scale must be positive and finite (PA_ERR_INVALID_ARG otherwise).
+ * Supported: BF16 pools, head_dim 64 or 128, block_size 16 or 32, num_heads /
+ *   num_kv_heads in {1, 2, 4, 8}; otherwise PA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------------- */
 int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                       int32_t num_heads, const int32_t* cu_seqlens_q,
