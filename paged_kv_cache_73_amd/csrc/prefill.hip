@@ -19,7 +19,8 @@
 //   l holds 16 scores of query row l%32 (the other 16 of the 32-key block sit in lane
 //   l^32).  The softmax is therefore lane-local apart from one exchange for the row max.
 //   O^T += V^T P^T then takes P straight from the S^T accumulators (the key order inside
-//   a 16-key step is permuted identically on both operands) and V^T from LDS.
+//   a 16-key step is permuted identically on both operands) and V^T from LDS, where V
+//   is stored transposed by the loader (a lane pair swaps halves of two keys' rows).
 // * The next tile's K/V are loaded into registers while the current tile is computed.
 // * Masking selects: keys past the request, beyond the causal limit or in a block whose
 //   id is outside [0, num_blocks) are set to -inf before the exponent; their K/V are
@@ -57,9 +58,12 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     constexpr int PER_THREAD = PIECES / kPrefillThreads;
     static_assert(PIECES % kPrefillThreads == 0, "tile split");
 
+    // V is stored transposed (V^T[d][key]) so that an O^T operand (8 keys of one dim) is
+    // two 8-byte reads.  Pitch BN + 2: 4-byte aligned rows, 2-way bank conflicts at most
+    // on the transposing writes.
+    constexpr int PITCH_T = BN + 2;
     __shared__ __align__(16) uint16_t k_lds[BN * PITCH];
-    __shared__ __align__(16) uint16_t v_lds[BN * PITCH];
-    __shared__ uint8_t key_ok[BN];
+    __shared__ __align__(16) uint16_t v_lds[D * PITCH_T];
 
     // Workgroups are handed to the 8 XCDs round-robin (id L runs on XCD L % 8).  All
     // query tiles of one (request, KV head) group read the same K/V pages, so they are
@@ -87,6 +91,10 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int lane = tid % kWave;
     const int w = tid / kWave;
     const int h = lane / 32;      // which 8-wide half of a 16-wide k-step this lane feeds
+    // Loader lanes lane and lane^CHUNKS hold keys 2k and 2k+1 of the same 8 dims.
+    const int par = (lane / CHUNKS) & 1;
+    const uint32_t sel_lo = par ? 0x01000504u : 0x05040100u;  // byte selectors: (even, odd) key
+    const uint32_t sel_hi = par ? 0x03020706u : 0x07060302u;  // low / high halves
     const int r = lane % 32;
     const int row = w * 32 + r;   // row of the workgroup this lane owns
     const int tok = tok0 + row / G;
@@ -136,7 +144,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // (past the end, or an id outside the pool) loads from the pool's first row and is
     // replaced by zeros.
     uint4 kr[PER_THREAD], vr[PER_THREAD];
-    bool okr[PER_THREAD], ldr[PER_THREAD];
+    bool ldr[PER_THREAD];
     auto fetch = [&](int t) {
         const int j0 = t * BN;
 #pragma unroll
@@ -153,19 +161,34 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             kr[u] = *reinterpret_cast<const uint4*>(k_cache + off);
             vr[u] = *reinterpret_cast<const uint4*>(v_cache + off);
             ldr[u] = ok;
-            okr[u] = ok || j >= kv_end;  // false only for an unassigned block inside the range
         }
     };
 
+    // Validity of the tile's pages (uniform): bit i set when page i of the tile is either
+    // past kv_end or holds a block id inside the pool.
+    constexpr int PAGES = BN / BS;
+    auto tile_pages_ok = [&](int t) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int i = 0; i < PAGES; ++i) {
+            const int jp = t * BN + i * BS;
+            const int32_t id = jp < kv_end ? table_row[jp / BS] : 0;
+            bits |= (static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks) ? 1u : 0u) << i;
+        }
+        return bits;
+    };
+    uint32_t ok_next = 0;
     if (n_tiles > 0) {
         fetch_ids(0);
         fetch(0);
+        ok_next = tile_pages_ok(0);
         if (n_tiles > 1) fetch_ids(1);
     }
     for (int t = 0; t < n_tiles; ++t) {
         const int j0 = t * BN;
         __syncthreads();  // the previous tile is no longer read
-        bool my_ok = true;
+        const uint32_t page_ok = ok_next;
+        const bool tile_ok = page_ok == (1u << PAGES) - 1;
 #pragma unroll
         for (int u = 0; u < PER_THREAD; ++u) {
             const int p = tid + u * kPrefillThreads;
@@ -174,13 +197,26 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             const uint4 z = make_uint4(0, 0, 0, 0);
             if (!ldr[u]) kr[u] = z, vr[u] = z;
             *reinterpret_cast<uint4*>(&k_lds[key * PITCH + chunk * 8]) = kr[u];
-            *reinterpret_cast<uint4*>(&v_lds[key * PITCH + chunk * 8]) = vr[u];
-            if (chunk == 0) key_ok[key] = okr[u];
-            my_ok = my_ok && okr[u];
+            {
+                // transpose through a lane pair: the even-key lane writes dims 0-3 of both
+                // keys, the odd-key lane dims 4-7, one 4-byte (two-key) word per dim
+                const uint32_t d0 = vr[u].x, d1 = vr[u].y, d2 = vr[u].z, d3 = vr[u].w;
+                const uint32_t send0 = par ? d0 : d2, send1 = par ? d1 : d3;
+                const uint32_t own0 = par ? d2 : d0, own1 = par ? d3 : d1;
+                const uint32_t rec0 = __shfl_xor(send0, CHUNKS), rec1 = __shfl_xor(send1, CHUNKS);
+                const int rb = chunk * 8 + 4 * par;
+                uint32_t* vt = reinterpret_cast<uint32_t*>(v_lds);
+                const int col = key / 2;
+                vt[((rb + 0) * PITCH_T) / 2 + col] = __builtin_amdgcn_perm(rec0, own0, sel_lo);
+                vt[((rb + 1) * PITCH_T) / 2 + col] = __builtin_amdgcn_perm(rec0, own0, sel_hi);
+                vt[((rb + 2) * PITCH_T) / 2 + col] = __builtin_amdgcn_perm(rec1, own1, sel_lo);
+                vt[((rb + 3) * PITCH_T) / 2 + col] = __builtin_amdgcn_perm(rec1, own1, sel_hi);
+            }
         }
-        const bool tile_ok = __syncthreads_and(my_ok);
+        __syncthreads();
         if (t + 1 < n_tiles) {  // in flight while this tile is computed
             fetch(t + 1);
+            ok_next = tile_pages_ok(t + 1);
             if (t + 2 < n_tiles) fetch_ids(t + 2);
         }
 
@@ -214,12 +250,14 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                     s[kb][x] = key <= lim ? s[kb][x] : -INFINITY;
                 }
             if (!tile_ok) {
+                // accumulator (kb, x) holds key 32kb + 8(x/4) + 4h + x%4; its page is
+                // (32kb + 8(x/4)) / BS for both lane halves, a compile-time index
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int x = 0; x < 16; ++x) {
-                        const int key = kb * 32 + 8 * (x / 4) + 4 * h + (x % 4);
-                        s[kb][x] = key_ok[key] ? s[kb][x] : -INFINITY;
+                        const int page = (kb * 32 + 8 * (x / 4)) / BS;
+                        s[kb][x] = (page_ok >> page) & 1u ? s[kb][x] : -INFINITY;
                     }
             }
         }
@@ -257,10 +295,9 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                u16x8_t a;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    a[e] = v_lds[(16 * ks + 4 * h + (e % 4) + 8 * (e / 4)) * PITCH + 32 * db + r];
+                const uint2 lo = *reinterpret_cast<const uint2*>(&v_lds[(32 * db + r) * PITCH_T + 16 * ks + 4 * h]);
+                const uint2 hi = *reinterpret_cast<const uint2*>(&v_lds[(32 * db + r) * PITCH_T + 16 * ks + 8 + 4 * h]);
+                const u16x8_t a = __builtin_bit_cast(u16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[ks], acc[db], 0, 0, 0);
             }
         }
