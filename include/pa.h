@@ -215,6 +215,22 @@ int pa_bm_prepare_write(pa_bm* bm, int32_t block_size, int32_t* row, int32_t wid
                         int32_t start, int32_t count, int32_t* cow_src, int32_t* cow_dst,
                         int32_t cow_capacity, int32_t* num_cow);
 
+/* Prefix cache ([NANO] 题目6: a block is looked up by compute_hash(token_ids, prefix_hash)
+ * in hash_to_block_id; a hit adds a reference, a miss allocates; a freed block leaves the
+ * map).  The page leaves compute_hash open; here it is FNV-1a 64 over the previous
+ * block's hash (8 bytes, little-endian) followed by the block's token ids (4 bytes each,
+ * little-endian), and the first block chains on 0. */
+uint64_t pa_prefix_block_hash(const int32_t* tokens, int32_t n, uint64_t prefix_hash);
+/* Table row for a request's n_tokens token ids: full block i is shared when its chained
+ * hash is registered and the block holds the same token ids (one more reference),
+ * otherwise a new block is taken and registered; the partial last block is always new
+ * and unregistered.  row[width] receives the ids (-1 past the end); *n_hits (nullable)
+ * the number of shared blocks, whose K/V need not be written again.  All or nothing
+ * (PA_ERR_OUT_OF_BLOCKS).  Blocks freed by pa_bm_decref / pa_bm_release_table leave the
+ * cache; a private registered block made writable by pa_bm_prepare_write leaves it too. */
+int pa_bm_allocate_prefix(pa_bm* bm, int32_t block_size, const int32_t* tokens,
+                          int32_t n_tokens, int32_t* row, int32_t width, int32_t* n_hits);
+
 /* slots_out[i] = table[seq[i]][pos[i] / B] * B + pos[i] % B, or -1 when that entry is
  * unassigned ([QWEN] 自己来实现: slot_mapping is computed once and reused by every
  * layer).  table: [*][width]; PA_ERR_INVALID_ARG when pos[i]/B >= width or seq[i] < 0. */

@@ -16,6 +16,11 @@ Pins (tests/test_oracle_pins.py):
 from __future__ import annotations
 
 
+FNV_OFFSET = 0xCBF29CE484222325
+FNV_PRIME = 0x100000001B3
+MASK64 = (1 << 64) - 1
+
+
 class OutOfBlocks(RuntimeError):
     pass
 
@@ -50,6 +55,11 @@ class BlockManager:
         self.num_blocks = num_blocks
         self.refs = [0] * num_blocks
         self.free = list(reversed(order))  # the top of the stack is the end of the list
+        # prefix cache (题目6): hash_to_block_id and, per registered block, its hash and
+        # the token ids it holds (checked on a hit)
+        self.hash_to_block = {}
+        self.block_hash = {}
+        self.block_tokens = {}
 
     def num_free(self) -> int:
         return len(self.free)
@@ -73,7 +83,57 @@ class BlockManager:
             raise RefcountError(f"block {block} is not allocated")
         self.refs[block] -= 1
         if self.refs[block] == 0:
+            self._forget(block)        # a freed block leaves hash_to_block_id (题目6, step 4)
             self.free.append(block)
+
+    def _forget(self, block: int) -> None:
+        h = self.block_hash.pop(block, None)
+        if h is not None:
+            del self.hash_to_block[h]
+            del self.block_tokens[block]
+
+    def allocate_prefix(self, tokens, block_size: int, width: int):
+        """Table row for a request's token ids, sharing cached full blocks (题目6).
+
+        Full block i gets the chained hash h_i = block_hash(tokens of block i, h_{i-1})
+        with h_{-1} = 0.  When h_i is in hash_to_block_id and the block holds the same
+        token ids, the block is shared (one more reference); otherwise a new block is
+        taken and registered under h_i.  The partial last block is always new and not
+        registered.  All or nothing.  Returns (row padded with -1, number of hits).
+        """
+        tokens = [int(t) for t in tokens]
+        n_full = len(tokens) // block_size
+        n_blocks = -(-len(tokens) // block_size)
+        if n_blocks > width:
+            raise ValueError("request longer than the table width")
+        plan, h = [], 0
+        for i in range(n_full):
+            chunk = tokens[i * block_size:(i + 1) * block_size]
+            h = block_hash(chunk, h)
+            hit = self.hash_to_block.get(h)
+            if hit is not None and self.block_tokens[hit] != chunk:
+                hit = None                  # a hash collision: not the same tokens
+            plan.append((h, chunk, hit))
+        misses = sum(1 for _, _, hit in plan if hit is None) + (n_blocks - n_full)
+        if misses > len(self.free):
+            raise OutOfBlocks(f"need {misses} blocks, {len(self.free)} free")
+        row, hits = [-1] * width, 0
+        for i, (h, chunk, hit) in enumerate(plan):
+            if hit is not None:
+                self.incref(hit)
+                row[i] = hit
+                hits += 1
+            else:
+                b = self.alloc(1)[0]
+                if h in self.hash_to_block:          # collision: the newer block takes the hash
+                    self._forget(self.hash_to_block[h])
+                self.hash_to_block[h] = b
+                self.block_hash[b] = h
+                self.block_tokens[b] = chunk
+                row[i] = b
+        if n_blocks > n_full:
+            row[n_full] = self.alloc(1)[0]
+        return row, hits
 
     def release_table(self, row) -> None:
         """End of a request: walk its table in reverse (题目6, step 4) and drop one
@@ -120,7 +180,29 @@ class BlockManager:
                 self.decref(old)
                 row[lb] = new
                 copies.append((old, new))
+            else:
+                self._forget(old)   # a private block about to change no longer matches its hash
         return copies
+
+
+# --------------------------------------------------------------------------------------
+# prefix-cache hash (题目6 leaves compute_hash open; this is FNV-1a 64, chained)
+# --------------------------------------------------------------------------------------
+
+def fnv1a64(data: bytes, h: int = FNV_OFFSET) -> int:
+    """FNV-1a, 64-bit: for each byte, xor it in, then multiply by the FNV prime."""
+    for byte in data:
+        h ^= byte
+        h = (h * FNV_PRIME) & MASK64
+    return h
+
+
+def block_hash(tokens, prefix_hash: int) -> int:
+    """Hash of one full block chained on the previous block's hash: FNV-1a 64 over the
+    previous hash (8 bytes, little-endian) followed by each token id (4 bytes, LE)."""
+    data = int(prefix_hash).to_bytes(8, "little") + b"".join(
+        int(t).to_bytes(4, "little", signed=True) for t in tokens)
+    return fnv1a64(data)
 
 
 # --------------------------------------------------------------------------------------

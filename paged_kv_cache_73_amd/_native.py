@@ -28,6 +28,7 @@ EXPORTS = [
     "pa_bm_alloc", "pa_bm_incref", "pa_bm_decref", "pa_bm_release_table", "pa_bm_share",
     "pa_bm_prepare_write", "pa_build_slot_mapping", "pa_build_cu_seqlens", "pa_pool_bytes",
     "pa_validate_decode", "pa_validate_varlen", "pa_validate_slots", "pa_probe_stream_read",
+    "pa_prefix_block_hash", "pa_bm_allocate_prefix",
 ]
 
 
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
                                               _I32, _I32P]),
         "pa_validate_slots": (ctypes.c_int, [_I32P, _I32, _I32, _I32, _I32P]),
         "pa_probe_stream_read": (ctypes.c_int, [_VP, ctypes.c_size_t, _VP, _I32, _VP]),
+        "pa_prefix_block_hash": (ctypes.c_uint64, [_I32P, _I32, ctypes.c_uint64]),
+        "pa_bm_allocate_prefix": (ctypes.c_int, [_VP, _I32, _I32P, _I32, _I32P, _I32, _I32P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -325,6 +328,16 @@ class BlockManager:
             _raise(st, "pa_bm_share")
         return out.tolist()
 
+    def allocate_prefix(self, tokens, block_size: int, width: int):
+        t = _i32(tokens)
+        row = np.full(max(1, width), -1, dtype=np.int32)
+        hits = ctypes.c_int32()
+        st = lib().pa_bm_allocate_prefix(self._h, block_size, _ptr(t), len(t), _ptr(row), width,
+                                         ctypes.byref(hits))
+        if st:
+            _raise(st, "pa_bm_allocate_prefix")
+        return row[:width].tolist(), hits.value
+
     def prepare_write(self, row: list, start: int, count: int, block_size: int):
         r = _i32(row)
         cap = len(r)
@@ -337,6 +350,11 @@ class BlockManager:
             _raise(st, "pa_bm_prepare_write")
         row[:] = r.tolist()
         return list(zip(src[:n.value].tolist(), dst[:n.value].tolist()))
+
+
+def pa_prefix_block_hash(tokens, prefix_hash: int) -> int:
+    t = _i32(tokens)
+    return int(lib().pa_prefix_block_hash(_ptr(t), len(t), prefix_hash))
 
 
 def pa_build_slot_mapping(table, block_size: int, seq, pos) -> np.ndarray:

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "pa.h"
@@ -17,7 +18,37 @@
 struct pa_bm {
     std::vector<int32_t> refs;   // reference count per physical block
     std::vector<int32_t> stack;  // free ids; back() is handed out next
+    // prefix cache ("结合nanovllm..." 题目6): hash_to_block_id, and per registered block its
+    // hash and the token ids it holds (compared on a hit)
+    std::unordered_map<uint64_t, int32_t> index;
+    std::vector<uint64_t> hash;
+    std::vector<uint8_t> hashed;
+    std::vector<std::vector<int32_t>> tokens;
 };
+
+namespace {
+
+constexpr uint64_t kFnvOffset = 0xCBF29CE484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001B3ull;
+
+// FNV-1a, 64-bit: for each byte, xor it in, then multiply by the FNV prime.
+uint64_t fnv1a(uint64_t h, const uint8_t* p, size_t n) {
+    for (size_t i = 0; i < n; ++i) {
+        h ^= p[i];
+        h *= kFnvPrime;
+    }
+    return h;
+}
+
+// Unregister a block from the prefix cache (freed, or about to be modified).
+void forget(pa_bm* bm, int32_t b) {
+    if (!bm->hashed[b]) return;
+    bm->index.erase(bm->hash[b]);
+    bm->hashed[b] = 0;
+    bm->tokens[b].clear();
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -44,6 +75,9 @@ int pa_bm_create(int32_t num_blocks, const int32_t* initial_order, pa_bm** out) 
     if (bm == nullptr) return PA_ERR_INVALID_ARG;
     bm->refs.assign(num_blocks, 0);
     bm->stack.resize(num_blocks);
+    bm->hash.assign(num_blocks, 0);
+    bm->hashed.assign(num_blocks, 0);
+    bm->tokens.resize(num_blocks);
     if (initial_order != nullptr) {
         std::vector<char> seen(num_blocks, 0);
         for (int32_t i = 0; i < num_blocks; ++i) {
@@ -110,7 +144,10 @@ int pa_bm_incref(pa_bm* bm, int32_t block) {
 int pa_bm_decref(pa_bm* bm, int32_t block) {
     if (bm == nullptr || !valid_id(bm, block)) return PA_ERR_INVALID_ARG;
     if (bm->refs[block] <= 0) return PA_ERR_REFCOUNT;  // double free
-    if (--bm->refs[block] == 0) bm->stack.push_back(block);
+    if (--bm->refs[block] == 0) {
+        forget(bm, block);  // a freed block leaves hash_to_block_id (题目6, step 4)
+        bm->stack.push_back(block);
+    }
     return PA_OK;
 }
 
@@ -182,9 +219,74 @@ int pa_bm_prepare_write(pa_bm* bm, int32_t block_size, int32_t* row, int32_t wid
             cow_src[k] = old;
             cow_dst[k] = fresh;
             ++k;
+        } else {
+            forget(bm, old);  // a private block about to change no longer matches its hash
         }
     }
     *num_cow = k;
+    return PA_OK;
+}
+
+uint64_t pa_prefix_block_hash(const int32_t* tokens, int32_t n, uint64_t prefix_hash) {
+    uint8_t buf[8];
+    for (int i = 0; i < 8; ++i) buf[i] = static_cast<uint8_t>(prefix_hash >> (8 * i));
+    uint64_t h = fnv1a(kFnvOffset, buf, 8);
+    for (int32_t t = 0; t < n; ++t) {
+        const uint32_t u = static_cast<uint32_t>(tokens[t]);
+        for (int i = 0; i < 4; ++i) buf[i] = static_cast<uint8_t>(u >> (8 * i));
+        h = fnv1a(h, buf, 4);
+    }
+    return h;
+}
+
+int pa_bm_allocate_prefix(pa_bm* bm, int32_t block_size, const int32_t* tokens, int32_t n_tokens,
+                          int32_t* row, int32_t width, int32_t* n_hits) {
+    if (bm == nullptr || row == nullptr || block_size <= 0 || n_tokens < 0 || width < 0 ||
+        (n_tokens > 0 && tokens == nullptr))
+        return PA_ERR_INVALID_ARG;
+    const int32_t n_full = n_tokens / block_size;
+    const int32_t n_blocks = (n_tokens + block_size - 1) / block_size;
+    if (n_blocks > width) return PA_ERR_INVALID_ARG;
+    // plan first (all or nothing): the chained hash of every full block and its hit
+    std::vector<uint64_t> hs(n_full);
+    std::vector<int32_t> hit(n_full, -1);
+    uint64_t h = 0;
+    int32_t misses = n_blocks - n_full;
+    for (int32_t i = 0; i < n_full; ++i) {
+        const int32_t* chunk = tokens + static_cast<int64_t>(i) * block_size;
+        h = pa_prefix_block_hash(chunk, block_size, h);
+        hs[i] = h;
+        auto it = bm->index.find(h);
+        if (it != bm->index.end() &&
+            bm->tokens[it->second].size() == static_cast<size_t>(block_size) &&
+            std::equal(chunk, chunk + block_size, bm->tokens[it->second].begin()))
+            hit[i] = it->second;
+        else
+            ++misses;
+    }
+    if (static_cast<size_t>(misses) > bm->stack.size()) return PA_ERR_OUT_OF_BLOCKS;
+    int32_t hits = 0;
+    for (int32_t j = 0; j < width; ++j) row[j] = -1;
+    for (int32_t i = 0; i < n_full; ++i) {
+        if (hit[i] >= 0) {
+            ++bm->refs[hit[i]];
+            row[i] = hit[i];
+            ++hits;
+            continue;
+        }
+        int32_t b;
+        pa_bm_alloc(bm, 1, &b);
+        auto it = bm->index.find(hs[i]);
+        if (it != bm->index.end()) forget(bm, it->second);  // collision: the newer block takes the hash
+        bm->index[hs[i]] = b;
+        bm->hash[b] = hs[i];
+        bm->hashed[b] = 1;
+        const int32_t* chunk = tokens + static_cast<int64_t>(i) * block_size;
+        bm->tokens[b].assign(chunk, chunk + block_size);
+        row[i] = b;
+    }
+    if (n_blocks > n_full) pa_bm_alloc(bm, 1, &row[n_full]);
+    if (n_hits) *n_hits = hits;
     return PA_OK;
 }
 

@@ -429,6 +429,43 @@ def test_prefix_refcount_example(golden):
     check_prefix_refcount_example(golden("prefix_refcount_example.json"))
 
 
+def test_fnv1a64_reference_vectors(golden):
+    for text, hexval in golden("fnv1a64_vectors.json")["vectors"]:
+        assert K.fnv1a64(text.encode()) == int(hexval, 16)
+    # the chained block hash is FNV-1a over (previous hash LE64, token ids LE32)
+    assert K.block_hash([], 0) == K.fnv1a64(bytes(8))
+    assert K.block_hash([1, -1], 5) == K.fnv1a64((5).to_bytes(8, "little") + b"\x01\0\0\0" + b"\xff" * 4)
+
+
+def check_prefix_cache_example(g, Manager=K.BlockManager):
+    """题目6 from token ids: the hash lookup decides sharing, not explicit calls."""
+    B = g["block_size"]
+    A_, B_, C_, D_, E_, F_, G_, H_ = range(1, 9)
+    bm = Manager(16)
+    base, hits = bm.allocate_prefix([A_, B_, C_, D_], B, 3)
+    assert base[:2] == g["printed_base"]["table"] and hits == 0
+    assert {str(i): bm.refs[i] for i in base[:2]} == g["printed_base"]["refs"]
+    r1, hits = bm.allocate_prefix([A_, B_, C_, D_, E_, F_], B, 3)
+    assert r1 == g["printed_after_request1"]["table"] and hits == 2
+    assert {str(i): bm.refs[i] for i in r1} == g["printed_after_request1"]["refs"]
+    r2, hits = bm.allocate_prefix([A_, B_, C_, D_, G_, H_], B, 3)
+    assert r2 == g["printed_after_request2"]["table"] and hits == 2
+    assert {str(i): bm.refs[i] for i in r2} == g["printed_after_request2"]["refs"]
+    bm.release_table(r1)
+    assert {str(i): bm.refs[i] for i in (0, 1, 3)} == g["printed_after_request1_ends"]["refs"]
+    assert bm.free[-1] == g["printed_after_request1_ends"]["freed"][0]
+    # block 2 left the cache: [E, F] misses now and takes the freed block again
+    r3, hits = bm.allocate_prefix([A_, B_, C_, D_, E_, F_], B, 3)
+    assert r3 == [0, 1, 2] and hits == 2
+    # the same tokens after a different prefix do not hit (the hash is chained)
+    r4, hits = bm.allocate_prefix([G_, H_, E_, F_], B, 2)
+    assert hits == 0 and r4[1] != 2
+
+
+def test_prefix_cache_example(golden):
+    check_prefix_cache_example(golden("prefix_refcount_example.json"))
+
+
 def test_waste_and_growth(golden):
     g = golden("waste_example.json")
     alloc, waste = K.contiguous_waste(g["used"], g["max_len"])
@@ -557,6 +594,13 @@ def test_planted_mistakes_are_caught(monkeypatch, golden):
         return out
     _caught(monkeypatch, A, "prefill_varlen", top_left, check_chunked_prefill_equals_one_shot)
     # the freed block is appended at the bottom of the free stack
+    # the prefix hash ignores the chaining
+    with monkeypatch.context() as m:
+        m.setattr(K, "block_hash", lambda tokens, prefix: K.fnv1a64(b"".join(
+            int(t).to_bytes(4, "little", signed=True) for t in tokens)))
+        with pytest.raises(AssertionError):
+            check_prefix_cache_example(golden("prefix_refcount_example.json"))
+
     class BottomFree(K.BlockManager):
         def decref(self, block):
             self.refs[block] -= 1
