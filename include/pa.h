@@ -141,6 +141,24 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
               void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Decode with the KV write fused in ([HFPA] Çözme yolu: the decode kernel reads the cache
+ * through block_table and updates it in place).  Same arguments and result as
+ * pa_decode, plus k_new, v_new: device [batch][Hkv][d], the current token's K and V.
+ * For each sequence with n = seqlens_k[b] >= 1 they are stored at position n-1 (block
+ * block_table[b][(n-1)/B], slot (n-1)%B) and the n keys, that one included, are
+ * attended.  The position's block must be private and assigned (pa_bm_prepare_write,
+ * then pa_copy_blocks for its copy-on-write pairs); if its id is outside the pool the
+ * row is neither stored nor attended.  Equivalent to pa_write_kv with those slots
+ * followed by pa_decode, in one launch fewer.
+ * ------------------------------------------------------------------------------- */
+int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q, const void* k_new,
+                     const void* v_new, int32_t batch, int32_t num_heads,
+                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* seqlens_k, int32_t max_seqlen_k, float softmax_scale,
+                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Varlen (packed) prefill with a paged cache ([QWEN] fast-attn 库的使用:
  * flash_attn_varlen_func(q, k_cache, v_cache, max_seqlen_q, cu_seqlens_q, max_seqlen_k,
  * cu_seqlens_k, scale, causal, block_table); [HFPA] Değişken uzunluklu yol).

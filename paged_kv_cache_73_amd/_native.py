@@ -28,7 +28,7 @@ EXPORTS = [
     "pa_bm_alloc", "pa_bm_incref", "pa_bm_decref", "pa_bm_release_table", "pa_bm_share",
     "pa_bm_prepare_write", "pa_build_slot_mapping", "pa_build_cu_seqlens", "pa_pool_bytes",
     "pa_validate_decode", "pa_validate_varlen", "pa_validate_slots", "pa_probe_stream_read",
-    "pa_prefix_block_hash", "pa_bm_allocate_prefix",
+    "pa_prefix_block_hash", "pa_bm_allocate_prefix", "pa_decode_append",
 ]
 
 
@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7),
         "pa_decode": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP, _I32, _VP,
                                      _I32, ctypes.c_float, _I32, _VP, ctypes.c_size_t, _VP]),
+        "pa_decode_append": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _VP, _VP, _I32, _I32, _VP,
+                                            _I32, _VP, _I32, ctypes.c_float, _I32, _VP,
+                                            ctypes.c_size_t, _VP]),
         "pa_prefill_varlen": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP, _VP,
                                              _I32, _I32, _VP, _I32, ctypes.c_float, _I32, _VP]),
         "pa_bm_create": (ctypes.c_int, [_I32, _I32P, ctypes.POINTER(_VP)]),
@@ -229,6 +232,21 @@ def pa_decode(pool: KVPool, out, q, block_table, seqlens_k, max_seqlen_k: int,
                          _stream(stream))
     if st:
         _raise(st, "pa_decode")
+
+
+def pa_decode_append(pool: KVPool, out, q, k_new, v_new, block_table, seqlens_k,
+                     max_seqlen_k: int, softmax_scale: float, partition_tokens: int = 0,
+                     workspace=None, stream=None) -> None:
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pa_decode_append(ctypes.byref(pool.struct), _dev(out, "out"), _dev(q, "q"),
+                                _dev(k_new, "k_new"), _dev(v_new, "v_new"), batch, hq,
+                                _meta(block_table, "block_table"), int(block_table.shape[1]),
+                                _meta(seqlens_k, "seqlens_k"), int(max_seqlen_k),
+                                float(softmax_scale), int(partition_tokens),
+                                _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    if st:
+        _raise(st, "pa_decode_append")
 
 
 def pa_prefill_varlen(pool: KVPool, out, q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,

@@ -97,8 +97,9 @@ __device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[E], int
 
 template <typename T, int D, int BS, int G>
 __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_partial_kernel(
-    const T* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const T* __restrict__ q, char* k_cache, char* v_cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
+    const T* __restrict__ k_new, const T* __restrict__ v_new,
     T* __restrict__ out, float* __restrict__ o_part, float* __restrict__ ml_part,
     int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks, int32_t max_blocks,
     int32_t max_parts, int32_t part_pages, float qscale) {
@@ -137,6 +138,26 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
         for (int e = 0; e < E; ++e) qv[g][e] *= qscale;
     }
 
+    // Fused append (k_new != null): the current token sits at position seqlen - 1.  The
+    // workgroup of the last partition stores its K/V row in the cache and, when it
+    // consumes that page, takes the row from registers rather than from memory.
+    const int32_t* table_row = block_table + static_cast<int64_t>(b) * max_blocks;
+    const bool appending = k_new != nullptr && seqlen > 0 && part == n_parts - 1;
+    const int32_t new_pos = seqlen - 1;
+    uint4 nk = make_uint4(0, 0, 0, 0), nv = make_uint4(0, 0, 0, 0);
+    if (appending) {
+        const int64_t nrow = (static_cast<int64_t>(b) * num_kv_heads + hkv) * D + c * E;
+        nk = *reinterpret_cast<const uint4*>(k_new + nrow);
+        nv = *reinterpret_cast<const uint4*>(v_new + nrow);
+        const int32_t id = table_row[new_pos / BS];
+        if (r0 == 0 && id >= 0 && id < num_blocks) {
+            const int64_t off = ((static_cast<int64_t>(id) * BS + new_pos % BS) * num_kv_heads + hkv) *
+                                    S::kRowBytes + c * 16;
+            *reinterpret_cast<uint4*>(k_cache + off) = nk;
+            *reinterpret_cast<uint4*>(v_cache + off) = nv;
+        }
+    }
+
     float m[G], l[G], o[G][E];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -150,7 +171,6 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     // byte offset of this lane's first piece inside a page, and the step between loads
     const int32_t lane_off = (r0 * num_kv_heads + hkv) * S::kRowBytes + c * 16;
     const int32_t load_step = RPL * num_kv_heads * S::kRowBytes;
-    const int32_t* table_row = block_table + static_cast<int64_t>(b) * max_blocks;
 
     // Consume one page of K/V already in registers.  A page whose block id is outside
     // [0, num_blocks) was loaded from block 0 instead and is masked entirely.  Values are
@@ -158,11 +178,17 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     auto consume = [&](int32_t id, int32_t tok0, const uint4 (&kb)[NL], const uint4 (&vb)[NL]) {
         const bool valid = id >= 0 && id < num_blocks;
         const bool partial = !valid || tok0 + BS > t_end;
+        const bool has_new = appending && tok0 + BS > new_pos;  // uniform: the last page
+        auto piece = [&](const uint4 (&buf)[NL], const uint4& fresh, int j) {
+            uint4 x = buf[j];
+            if (has_new && tok0 + r0 + j * RPL == new_pos) x = fresh;
+            return x;
+        };
         float s[G][NL];
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             float kf[E];
-            widen(kb[j], kf, T{});
+            widen(piece(kb, nk, j), kf, T{});
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float acc = 0.f;
@@ -204,7 +230,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             float vf[E];
-            widen(vb[j], vf, T{});
+            widen(piece(vb, nv, j), vf, T{});
             if (partial) {  // a masked row may hold anything (NaN): select, never multiply
 #pragma unroll
                 for (int e = 0; e < E; ++e) vf[e] = ok[j] ? vf[e] : 0.f;
@@ -382,15 +408,16 @@ inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size, int3
 template <typename T, int D, int BS, int G>
 int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                   int32_t num_heads, const int32_t* table, int32_t max_blocks,
-                  const int32_t* seqlens, int32_t max_parts, int32_t part_tokens, float scale,
-                  float* o_part, float* ml_part, hipStream_t stream) {
+                  const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
+                  int32_t part_tokens, float scale, float* o_part, float* ml_part, hipStream_t stream) {
     const int hkv = pool->num_kv_heads;
     int per_wg = PA_DECODE_HPW;
     while (hkv % per_wg != 0) per_wg >>= 1;
     const dim3 grid(hkv / per_wg, max_parts, batch);
     hipLaunchKernelGGL((decode_partial_kernel<T, D, BS, G>), grid, dim3(per_wg * kWave), 0, stream,
-                       static_cast<const T*>(q), static_cast<const char*>(pool->k_cache),
-                       static_cast<const char*>(pool->v_cache), table, seqlens,
+                       static_cast<const T*>(q), static_cast<char*>(pool->k_cache),
+                       static_cast<char*>(pool->v_cache), table, seqlens,
+                       static_cast<const T*>(k_new), static_cast<const T*>(v_new),
                        static_cast<T*>(out), o_part, ml_part, num_heads, hkv, pool->num_blocks,
                        max_blocks, max_parts, part_tokens / BS, scale * kLog2e);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
@@ -405,13 +432,14 @@ int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batc
 template <typename T, int D, int BS>
 int dispatch_group(int G, const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                    int32_t num_heads, const int32_t* table, int32_t max_blocks,
-                   const int32_t* seqlens, int32_t max_parts, int32_t part_tokens, float scale,
-                   float* o_part, float* ml_part, hipStream_t stream) {
+                   const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
+                   int32_t part_tokens, float scale, float* o_part, float* ml_part,
+                   hipStream_t stream) {
 #define PA_DECODE_G(GG)                                                                    \
     case GG:                                                                               \
         return launch_decode<T, D, BS, GG>(pool, out, q, batch, num_heads, table, max_blocks, \
-                                           seqlens, max_parts, part_tokens, scale, o_part,   \
-                                           ml_part, stream);
+                                           seqlens, k_new, v_new, max_parts, part_tokens,    \
+                                           scale, o_part, ml_part, stream);
     switch (G) {
         PA_DECODE_G(1)
         PA_DECODE_G(2)
@@ -425,14 +453,15 @@ int dispatch_group(int G, const pa_kv_pool* pool, void* out, const void* q, int3
 template <typename T>
 int dispatch_shape(int G, const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                    int32_t num_heads, const int32_t* table, int32_t max_blocks,
-                   const int32_t* seqlens, int32_t max_parts, int32_t part_tokens, float scale,
-                   float* o_part, float* ml_part, hipStream_t stream) {
+                   const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
+                   int32_t part_tokens, float scale, float* o_part, float* ml_part,
+                   hipStream_t stream) {
     const int D = pool->head_dim, BS = pool->block_size;
 #define PA_DECODE_SHAPE(DD, BB)                                                             \
     if (D == DD && BS == BB)                                                                \
         return dispatch_group<T, DD, BB>(G, pool, out, q, batch, num_heads, table, max_blocks, \
-                                         seqlens, max_parts, part_tokens, scale, o_part,      \
-                                         ml_part, stream);
+                                         seqlens, k_new, v_new, max_parts, part_tokens,       \
+                                         scale, o_part, ml_part, stream);
     PA_DECODE_SHAPE(64, 16)
     PA_DECODE_SHAPE(64, 32)
     PA_DECODE_SHAPE(128, 16)
@@ -464,12 +493,13 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads,
     return workspace_bytes(batch, num_heads, head_dim, num_parts(max_seqlen_k, p));
 }
 
-extern "C" int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
-                         int32_t num_heads, const int32_t* block_table,
-                         int32_t max_blocks_per_seq, const int32_t* seqlens_k,
-                         int32_t max_seqlen_k, float softmax_scale, int32_t partition_tokens,
-                         void* workspace, size_t workspace_size, void* stream) {
-    using namespace pa;
+namespace pa {
+
+int decode_impl(const pa_kv_pool* pool, void* out, const void* q, const void* k_new,
+                const void* v_new, int32_t batch, int32_t num_heads, const int32_t* block_table,
+                int32_t max_blocks_per_seq, const int32_t* seqlens_k, int32_t max_seqlen_k,
+                float softmax_scale, int32_t partition_tokens, void* workspace,
+                size_t workspace_size, void* stream) {
     int st = check_pool(pool);
     if (st != PA_OK) return st;
     if (batch < 0 || num_heads <= 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0 ||
@@ -500,9 +530,34 @@ extern "C" int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (pool->dtype == PA_BF16)
         return dispatch_shape<bf16_t>(G, pool, out, q, batch, num_heads, block_table,
-                                      max_blocks_per_seq, seqlens_k, max_parts, part_tokens,
-                                      softmax_scale, o_part, ml_part, s);
+                                      max_blocks_per_seq, seqlens_k, k_new, v_new, max_parts,
+                                      part_tokens, softmax_scale, o_part, ml_part, s);
     return dispatch_shape<float>(G, pool, out, q, batch, num_heads, block_table,
-                                 max_blocks_per_seq, seqlens_k, max_parts, part_tokens,
-                                 softmax_scale, o_part, ml_part, s);
+                                 max_blocks_per_seq, seqlens_k, k_new, v_new, max_parts,
+                                 part_tokens, softmax_scale, o_part, ml_part, s);
+}
+
+}  // namespace pa
+
+extern "C" int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                         int32_t num_heads, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* seqlens_k,
+                         int32_t max_seqlen_k, float softmax_scale, int32_t partition_tokens,
+                         void* workspace, size_t workspace_size, void* stream) {
+    return pa::decode_impl(pool, out, q, nullptr, nullptr, batch, num_heads, block_table,
+                           max_blocks_per_seq, seqlens_k, max_seqlen_k, softmax_scale,
+                           partition_tokens, workspace, workspace_size, stream);
+}
+
+extern "C" int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q,
+                                const void* k_new, const void* v_new, int32_t batch,
+                                int32_t num_heads, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, const int32_t* seqlens_k,
+                                int32_t max_seqlen_k, float softmax_scale,
+                                int32_t partition_tokens, void* workspace, size_t workspace_size,
+                                void* stream) {
+    if (batch > 0 && (k_new == nullptr || v_new == nullptr)) return PA_ERR_INVALID_ARG;
+    return pa::decode_impl(pool, out, q, k_new, v_new, batch, num_heads, block_table,
+                           max_blocks_per_seq, seqlens_k, max_seqlen_k, softmax_scale,
+                           partition_tokens, workspace, workspace_size, stream);
 }

@@ -3,7 +3,8 @@
 Set-up (not part of a step): the library's block manager plans the tables and slots,
 the pools are filled with NaN, and the cached context is written with pa_write_kv.
 A step is the hot path of one layer: pa_copy_blocks for the copy-on-write pairs (if
-any), pa_write_kv for the new tokens, then pa_decode or pa_prefill_varlen.
+any), pa_write_kv for the new tokens, then pa_decode or pa_prefill_varlen.  A fused
+decode step replaces the last two by pa_decode_append.
 """
 
 from __future__ import annotations
@@ -87,7 +88,23 @@ def attend(w: W.Workload, r: DeviceRun, partition_tokens: int = 0) -> None:
                              r.table, w.scale, w.causal)
 
 
-def step(w: W.Workload, r: DeviceRun, partition_tokens: int = 0, attention: bool = True) -> None:
+def attend_append(w: W.Workload, r: DeviceRun, partition_tokens: int = 0) -> None:
+    """Decode with the new tokens' K/V stored by the attention launch itself."""
+    if w.kind != "decode":
+        raise ValueError("the fused append is a decode step")
+    ensure_workspace(w, r, partition_tokens)
+    max_k = max(r.plan.seqlens_k) if r.plan.seqlens_k else 0
+    pa.pa_decode_append(r.pool, r.out, r.q, r.k_new, r.v_new, r.table, r.seqlens, max_k,
+                        w.scale, partition_tokens, r.workspace)
+
+
+def step(w: W.Workload, r: DeviceRun, partition_tokens: int = 0, attention: bool = True,
+         fused: bool = False) -> None:
+    if fused:
+        if r.copy_src.numel():
+            pa.pa_copy_blocks(r.pool, r.copy_src, r.copy_dst)
+        attend_append(w, r, partition_tokens)
+        return
     write(w, r)
     if attention:
         attend(w, r, partition_tokens)

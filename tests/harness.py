@@ -80,8 +80,9 @@ def gpu_setup(w: W.Workload, dev="cuda") -> R.DeviceRun:
     return R.setup(w, dev)
 
 
-def gpu_step(w: W.Workload, g: R.DeviceRun, partition_tokens: int = 0, attention: bool = True):
-    R.step(w, g, partition_tokens, attention)
+def gpu_step(w: W.Workload, g: R.DeviceRun, partition_tokens: int = 0, attention: bool = True,
+             fused: bool = False):
+    R.step(w, g, partition_tokens, attention, fused)
 
 
 def pool_bits(t: torch.Tensor, dtype: str) -> np.ndarray:

@@ -214,6 +214,91 @@ def test_decode_workspace_and_argument_errors():
 
 
 # --------------------------------------------------------------------------------------
+# decode with the KV write fused in
+# --------------------------------------------------------------------------------------
+
+FUSED_CASES = [  # (cached lengths, dtype, Hq, Hkv, d, B, partition tokens)
+    ([0, 1, 15, 16, 17, 31, 32, 100], "bf16", 16, 8, 128, 16, 0),
+    ([0, 1, 15, 16, 17, 31, 32, 100], "bf16", 16, 8, 128, 16, 32),
+    ([5, 63, 64, 700, 1023], "bf16", 16, 2, 64, 32, 64),
+    ([3, 16, 40, 129], "f32", 8, 4, 128, 16, 16),
+    ([0, 31, 32, 500], "f32", 4, 1, 64, 32, 0),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: f"{c[1]}-{c[2]}-{c[3]}-{c[4]}-{c[5]}-P{c[6]}")
+def test_decode_append_matches_write_then_decode(case):
+    cached, dtype, hq, hkv, d, B, p = case
+    w = W.decode_workload(cached, dtype=dtype, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                          block_size=B, seed=21)
+    sep, fus = H.gpu_setup(w), H.gpu_setup(w)
+    H.gpu_step(w, sep, p)
+    H.gpu_step(w, fus, p, fused=True)
+    torch.cuda.synchronize()
+    o = H.oracle_run(w)
+    # the cache after the fused call is the one the oracle writes, bit for bit
+    assert np.array_equal(H.pool_bits(fus.k_cache, w.dtype).view(np.uint8), o.k_pool.view(np.uint8))
+    assert np.array_equal(H.pool_bits(fus.v_cache, w.dtype).view(np.uint8), o.v_pool.view(np.uint8))
+    # the output is the separate path's, bit for bit (same keys, same arithmetic order)
+    assert torch.equal(fus.out, sep.out)
+    H.assert_close(H.out_f64(fus.out), o.out, w.dtype, f"fused {case}")
+
+
+def test_decode_append_qwen3_b64_full_and_copy_on_write():
+    w = W.qwen3_decode(seed=1)
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g, 0, fused=True)
+    torch.cuda.synchronize()
+    o = H.oracle_run(w)
+    H.assert_close(H.out_f64(g.out), o.out, w.dtype, "fused qwen3 b64")
+    assert np.array_equal(H.pool_bits(g.k_cache, w.dtype).view(np.uint8), o.k_pool.view(np.uint8))
+    # a shared prefix: the new token's block is a fresh copy made by pa_copy_blocks first
+    w = W.shared_prefix_decode(seed=2, groups=2, per_group=4, prefix_len=64, suffix_lo=5,
+                               suffix_hi=40)
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g, 0, fused=True)
+    torch.cuda.synchronize()
+    o = H.oracle_run(w)
+    H.assert_close(H.out_f64(g.out), o.out, w.dtype, "fused shared prefix")
+    assert np.array_equal(H.pool_bits(g.v_cache, w.dtype).view(np.uint8), o.v_pool.view(np.uint8))
+
+
+def test_decode_append_edge_cases():
+    w = W.decode_workload([0, 40, 7], dtype="bf16", num_heads=16, num_kv_heads=8, head_dim=128,
+                          block_size=16, seed=22)
+    g = H.gpu_setup(w)
+    before_k = H.pool_bits(g.k_cache, w.dtype)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    # a sequence of length 0 stores nothing and gives zeros; batch 0 is a no-op
+    zero = torch.zeros_like(g.seqlens)
+    g.out.fill_(7)
+    pa.pa_decode_append(g.pool, g.out, g.q, g.k_new, g.v_new, g.table, zero, 0, w.scale, 0, ws)
+    pa.pa_decode_append(g.pool, g.out[:0], g.q[:0], g.k_new[:0], g.v_new[:0], g.table[:0],
+                        zero[:0], 0, w.scale, 0, ws)
+    torch.cuda.synchronize()
+    assert not g.out.float().abs().sum().item()
+    assert np.array_equal(H.pool_bits(g.k_cache, w.dtype), before_k)
+    # the new position's block outside the pool: neither stored nor attended
+    table = g.table.clone()
+    table[1, 40 // 16] = 10 ** 6
+    pa.pa_decode_append(g.pool, g.out, g.q, g.k_new, g.v_new, table, g.seqlens, 41, w.scale, 0, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.pool_bits(g.k_cache, w.dtype)[table.cpu().numpy()[1, :2]],
+                          before_k[table.cpu().numpy()[1, :2]])
+    from oracle import attention as OA
+    o = H.oracle_run(w, attention=False)
+    ref_table = np.asarray(g.plan.tables).copy()
+    ref_table[1, 40 // 16] = -1
+    ref = OA.decode(H.storage(w.q, w.dtype), o.k_pool, o.v_pool, ref_table, g.plan.seqlens_k,
+                    w.scale, w.dtype)
+    H.assert_close(H.out_f64(g.out)[1:2], ref[1:2], w.dtype, "fused, new block outside the pool")
+    # missing k_new / v_new is an argument error
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_append(g.pool, g.out, g.q, None, g.v_new, g.table, g.seqlens, 41, w.scale, 0, ws)
+    assert e.value.code == -1
+
+
+# --------------------------------------------------------------------------------------
 # the full-size workloads
 # --------------------------------------------------------------------------------------
 
