@@ -185,6 +185,24 @@ int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t 
                       void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Varlen prefill over contiguous (non-paged) K/V ([QWEN] fast-attn 库的使用: the same
+ * varlen call without block_table, k and v then being packed like q; [HFPA]
+ * Değişken uzunluklu yol).  The choice when nothing is cached yet.
+ *
+ * k, v: device, [total_k][num_kv_heads][head_dim] with total_k = cu_seqlens_k[batch];
+ *   request i's keys are rows [cu_k[i], cu_k[i+1]).  q, out: [total_q][num_heads]
+ *   [head_dim] as for pa_prefill_varlen; dtype: PA_BF16 (PA_F32 returns
+ *   PA_ERR_UNSUPPORTED).  Masking, alignment, scale and supported shapes as for
+ *   pa_prefill_varlen.  Nothing is owned or kept by the library.
+ * ------------------------------------------------------------------------------- */
+int pa_prefill_varlen_contiguous(void* out, const void* q, const void* k, const void* v,
+                                 int32_t dtype, int32_t batch, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                                 int32_t causal, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Measurement helper (not part of the attention path): reads `bytes` (a multiple of 16)
  * of device memory at `buf` with non-temporal 16-byte loads from `grid` workgroups of
  * 256 threads, as a plain streaming read; `sink` is a device word that is normally

@@ -17,6 +17,10 @@ Pins (tests/test_oracle_pins.py):
                               equals dense attention.  The causal alignment with a
                               cached prefix is a reading (bottom-right), pinned only
                               by those invariants.
+  * prefill_varlen_contiguous -- torch's float64 scaled-dot-product attention when
+                              nothing is cached (causal and not), chunked equals
+                              one-shot, and equal to prefill_varlen on the same keys
+                              scattered into a shuffled paged pool.
   * merge_states           -- any split of the keys merges to the one-shot result.
 """
 
@@ -213,6 +217,35 @@ def prefill_varlen(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, cu_seq
             for h in range(hq):
                 out[row, h] = attend(qf[row, h], kf[:n_visible, h // group],
                                      vf[:n_visible, h // group], scale)
+    return out
+
+
+def prefill_varlen_contiguous(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_q,
+                              cu_seqlens_k, scale: float, causal: bool, dtype: str) -> np.ndarray:
+    """Packed (varlen) prefill with contiguous keys: the same call without a block
+    table ("从零开始写Qwen3（六）", fast-attn 库的使用; "Sayfalı dikkat", Değişken uzunluklu
+    yol), so k and v are packed like q, ``[sum_k, Hkv, d]``, and request i's keys are
+    rows [cu_k[i], cu_k[i+1]).  Visibility as in prefill_varlen: with c = k_len - q_len,
+    query row t sees keys j <= c + t when causal, all keys otherwise; no key -> zeros.
+    """
+    total_q, hq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    qf, kf, vf = to_f64(q, dtype), to_f64(k, dtype), to_f64(v, dtype)
+    cu_q = np.asarray(cu_seqlens_q, dtype=np.int64)
+    cu_k = np.asarray(cu_seqlens_k, dtype=np.int64)
+    out = np.zeros((total_q, hq, d), dtype=np.float64)
+    for i in range(len(cu_q) - 1):
+        q_len = int(cu_q[i + 1] - cu_q[i])
+        k0, k_len = int(cu_k[i]), int(cu_k[i + 1] - cu_k[i])
+        cached = k_len - q_len
+        for t in range(q_len):
+            n_visible = min(max(cached + t + 1, 0), k_len) if causal else k_len
+            row = int(cu_q[i]) + t
+            keys = kf[k0:k0 + n_visible]
+            vals = vf[k0:k0 + n_visible]
+            for h in range(hq):
+                out[row, h] = attend(qf[row, h], keys[:, h // group], vals[:, h // group], scale)
     return out
 
 

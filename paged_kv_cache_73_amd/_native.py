@@ -29,6 +29,7 @@ EXPORTS = [
     "pa_bm_prepare_write", "pa_build_slot_mapping", "pa_build_cu_seqlens", "pa_pool_bytes",
     "pa_validate_decode", "pa_validate_varlen", "pa_validate_slots", "pa_probe_stream_read",
     "pa_prefix_block_hash", "pa_bm_allocate_prefix", "pa_decode_append",
+    "pa_prefill_varlen_contiguous",
 ]
 
 
@@ -89,6 +90,9 @@ def lib() -> ctypes.CDLL:
                                             ctypes.c_size_t, _VP]),
         "pa_prefill_varlen": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP, _VP,
                                              _I32, _I32, _VP, _I32, ctypes.c_float, _I32, _VP]),
+        "pa_prefill_varlen_contiguous": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
+                                                        _I32, _VP, _VP, _I32, _I32, ctypes.c_float,
+                                                        _I32, _VP]),
         "pa_bm_create": (ctypes.c_int, [_I32, _I32P, ctypes.POINTER(_VP)]),
         "pa_bm_destroy": (None, [_VP]),
         "pa_bm_num_free": (_I32, [_VP]),
@@ -261,6 +265,26 @@ def pa_prefill_varlen(pool: KVPool, out, q, cu_seqlens_q, cu_seqlens_k, max_seql
                                  _stream(stream))
     if st:
         _raise(st, "pa_prefill_varlen")
+
+
+def pa_prefill_varlen_contiguous(out, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                                 max_seqlen_k: int, softmax_scale: float, causal: bool = True,
+                                 stream=None) -> None:
+    """Packed q [total_q, Hq, d] against packed k, v [total_k, Hkv, d] (no block table)."""
+    torch = _torch()
+    if k.shape != v.shape or k.dtype != v.dtype or k.dtype != q.dtype or k.dim() != 3:
+        raise ValueError("k and v must both be [total_k, Hkv, d] of q's dtype")
+    dt = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    batch = int(cu_seqlens_q.shape[0]) - 1
+    st = lib().pa_prefill_varlen_contiguous(
+        _dev(out, "out"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), dt, batch, int(q.shape[1]),
+        int(k.shape[1]), int(k.shape[2]), _meta(cu_seqlens_q, "cu_seqlens_q"),
+        _meta(cu_seqlens_k, "cu_seqlens_k"), int(max_seqlen_q), int(max_seqlen_k),
+        float(softmax_scale), int(bool(causal)), _stream(stream))
+    if st:
+        _raise(st, "pa_prefill_varlen_contiguous")
 
 
 def pa_probe_stream_read(buf, sink, grid: int, stream=None) -> None:

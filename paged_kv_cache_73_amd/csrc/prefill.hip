@@ -25,6 +25,10 @@
 // * Masking selects: keys past the request, beyond the causal limit or in a block whose
 //   id is outside [0, num_blocks) are set to -inf before the exponent; their K/V are
 //   loaded as zeros (never from the pool), so no NaN can enter the products.
+// * BS = 0 instantiates the same kernel for contiguous K/V (the varlen call without a
+//   block table, "从零开始写Qwen3（六）" fast-attn 库的使用): request i's keys are rows
+//   [cu_k[i], cu_k[i+1]) of packed [sum_k][Hkv][d] arrays, and only the addressing of
+//   the loader differs.
 
 #include <algorithm>
 
@@ -41,7 +45,7 @@ constexpr int kPrefillKeys = 64;    // keys per tile
 constexpr int kPrefillThreads = 256;
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X
 
-template <int D, int G, int BS>
+template <int D, int G, int BS>  // BS = 0: contiguous K/V
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ cu_q,
@@ -49,6 +53,8 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     uint16_t* __restrict__ out, int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks,
     int32_t max_blocks, float qscale, int32_t causal, int32_t n_qtiles, int32_t n_groups) {
     constexpr int BN = kPrefillKeys;
+    constexpr bool kPaged = BS > 0;
+    constexpr int PBS = kPaged ? BS : BN;        // keys per page (one page per tile when contiguous)
     constexpr int TOK = kPrefillRows / G;       // tokens per workgroup
     constexpr int KS = D / 16;                  // MFMA k-steps over the head dim
     constexpr int DB = D / 32;                  // 32-wide blocks of the head dim in O^T
@@ -82,10 +88,10 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     if (tok0 >= q_len) return;  // uniform: tile past this request's queries
     const int k_len_req = cu_k[req + 1] - cu_k[req];
     const int cached = k_len_req - q_len;                       // may be negative
-    const int k_len = min(k_len_req, max_blocks * BS);  // keys past the table: never read
+    const int k_len = kPaged ? min(k_len_req, max_blocks * BS) : k_len_req;  // keys past the table: never read
     const int tok_last = min(tok0 + TOK, q_len) - 1;
     const int kv_end = causal ? min(k_len, cached + tok_last + 1) : k_len;
-    const int n_tiles = (kv_end > 0 && num_blocks > 0) ? (kv_end + BN - 1) / BN : 0;
+    const int n_tiles = (kv_end > 0 && (!kPaged || num_blocks > 0)) ? (kv_end + BN - 1) / BN : 0;
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -126,7 +132,8 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         for (int x = 0; x < 16; ++x) acc[db][x] = 0.f;
     float m = -INFINITY, l = 0.f;
 
-    const int32_t* table_row = block_table + static_cast<int64_t>(req) * max_blocks;
+    const int32_t* table_row = kPaged ? block_table + static_cast<int64_t>(req) * max_blocks : nullptr;
+    const int64_t key_base = kPaged ? 0 : cu_k[req];  // first packed row of the request (contiguous)
     const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * D * 2;  // bytes per slot
 
     // Block ids of this thread's pieces are loaded one tile before the K/V they address,
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int u = 0; u < PER_THREAD; ++u) {
             const int j = j0 + (tid + u * kPrefillThreads) / CHUNKS;
-            ids[u] = table_row[min(j, kv_end - 1) / BS];
+            ids[u] = kPaged ? table_row[min(j, kv_end - 1) / PBS] : 0;
         }
     };
     // global -> registers for one tile, without branches: a piece that must not be read
@@ -152,9 +159,11 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             const int p = tid + u * kPrefillThreads;
             const int j = j0 + p / CHUNKS;
             const int32_t id = ids[u];
-            const bool ok = j < kv_end && static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks);
-            const int64_t off = ok ? (static_cast<int64_t>(id) * BS + j % BS) * row_stride +
-                                         static_cast<int64_t>(hkv) * D * 2 + (p % CHUNKS) * 16
+            const bool ok = j < kv_end &&
+                            (!kPaged || static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks));
+            const int64_t key_row = kPaged ? static_cast<int64_t>(id) * PBS + j % PBS : key_base + j;
+            const int64_t off = ok ? key_row * row_stride + static_cast<int64_t>(hkv) * D * 2 +
+                                         (p % CHUNKS) * 16
                                    : 0;
             // consumed (and zeroed when !ok) only when stored to LDS in the next iteration,
             // so the loads stay in flight while the current tile is computed
@@ -166,13 +175,14 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 
     // Validity of the tile's pages (uniform): bit i set when page i of the tile is either
     // past kv_end or holds a block id inside the pool.
-    constexpr int PAGES = BN / BS;
+    constexpr int PAGES = BN / PBS;
     auto tile_pages_ok = [&](int t) {
         uint32_t bits = 0;
+        if (!kPaged) return 1u;
 #pragma unroll
         for (int i = 0; i < PAGES; ++i) {
-            const int jp = t * BN + i * BS;
-            const int32_t id = jp < kv_end ? table_row[jp / BS] : 0;
+            const int jp = t * BN + i * PBS;
+            const int32_t id = jp < kv_end ? table_row[jp / PBS] : 0;
             bits |= (static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks) ? 1u : 0u) << i;
         }
         return bits;
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int x = 0; x < 16; ++x) {
-                        const int page = (kb * 32 + 8 * (x / 4)) / BS;
+                        const int page = (kb * 32 + 8 * (x / 4)) / PBS;
                         s[kb][x] = (page_ok >> page) & 1u ? s[kb][x] : -INFINITY;
                     }
             }
@@ -320,40 +330,48 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         }
 }
 
+// Where the keys live: a paged pool (table != null) or packed contiguous arrays.
+struct KvSource {
+    bool paged;
+    const void* k;
+    const void* v;
+    int32_t num_kv_heads;
+    int32_t num_blocks;   // paged only
+    int32_t block_size;   // paged only
+    const int32_t* table; // paged only
+    int32_t max_blocks;   // paged only
+};
+
 template <int D, int G, int BS>
-int launch_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                    int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
-                   int32_t max_seqlen_q, const int32_t* table, int32_t max_blocks,
-                   float scale, int32_t causal, hipStream_t stream) {
+                   int32_t max_seqlen_q, float scale, int32_t causal, hipStream_t stream) {
     const int tok_per_wg = kPrefillRows / G;
     const int64_t n_qtiles = (max_seqlen_q + tok_per_wg - 1) / tok_per_wg;
-    const int64_t n_groups = static_cast<int64_t>(pool->num_kv_heads) * batch;
+    const int64_t n_groups = static_cast<int64_t>(kv.num_kv_heads) * batch;
     const int64_t padded = (n_groups + kXcds - 1) / kXcds * n_qtiles * kXcds;
     if (padded > INT32_MAX) return PA_ERR_UNSUPPORTED;
     const dim3 grid(static_cast<uint32_t>(padded));
     hipLaunchKernelGGL((prefill_kernel<D, G, BS>), grid, dim3(kPrefillThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const char*>(pool->k_cache),
-                       static_cast<const char*>(pool->v_cache), cu_q, cu_k, table,
-                       static_cast<uint16_t*>(out), num_heads, pool->num_kv_heads,
-                       pool->num_blocks, max_blocks, scale * kLog2e, causal,
+                       static_cast<const uint16_t*>(q), static_cast<const char*>(kv.k),
+                       static_cast<const char*>(kv.v), cu_q, cu_k, kv.table,
+                       static_cast<uint16_t*>(out), num_heads, kv.num_kv_heads,
+                       kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
                        static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups));
     return launch_status();
 }
 
 template <int D>
-int dispatch_prefill_group(int G, const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+int dispatch_prefill_group(int G, const KvSource& kv, void* out, const void* q, int32_t batch,
                            int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
-                           int32_t max_seqlen_q, const int32_t* table, int32_t max_blocks,
-                           float scale, int32_t causal, hipStream_t stream) {
+                           int32_t max_seqlen_q, float scale, int32_t causal,
+                           hipStream_t stream) {
+#define PA_PREFILL_LAUNCH(GG, BB) \
+    launch_prefill<D, GG, BB>(kv, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, scale, causal, stream)
 #define PA_PREFILL_CASE(GG)                                                                     \
     case GG:                                                                                    \
-        return pool->block_size == 16                                                          \
-                   ? launch_prefill<D, GG, 16>(pool, out, q, batch, num_heads, cu_q, cu_k,      \
-                                               max_seqlen_q, table, max_blocks, scale, causal,  \
-                                               stream)                                          \
-                   : launch_prefill<D, GG, 32>(pool, out, q, batch, num_heads, cu_q, cu_k,      \
-                                               max_seqlen_q, table, max_blocks, scale, causal,  \
-                                               stream);
+        if (!kv.paged) return PA_PREFILL_LAUNCH(GG, 0);                              \
+        return kv.block_size == 16 ? PA_PREFILL_LAUNCH(GG, 16) : PA_PREFILL_LAUNCH(GG, 32);
     switch (G) {
         PA_PREFILL_CASE(1)
         PA_PREFILL_CASE(2)
@@ -362,6 +380,22 @@ int dispatch_prefill_group(int G, const pa_kv_pool* pool, void* out, const void*
         default: return PA_ERR_UNSUPPORTED;
     }
 #undef PA_PREFILL_CASE
+#undef PA_PREFILL_LAUNCH
+}
+
+int prefill_impl(const KvSource& kv, int32_t head_dim, void* out, const void* q, int32_t batch,
+                 int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
+                 int32_t max_seqlen_q, float scale, int32_t causal, hipStream_t s) {
+    if (num_heads % kv.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || scale == INFINITY) return PA_ERR_INVALID_ARG;
+    const int G = num_heads / kv.num_kv_heads;
+    if (head_dim == 128)
+        return dispatch_prefill_group<128>(G, kv, out, q, batch, num_heads, cu_q, cu_k,
+                                           max_seqlen_q, scale, causal != 0, s);
+    if (head_dim == 64)
+        return dispatch_prefill_group<64>(G, kv, out, q, batch, num_heads, cu_q, cu_k,
+                                          max_seqlen_q, scale, causal != 0, s);
+    return PA_ERR_UNSUPPORTED;
 }
 
 }  // namespace pa
@@ -382,20 +416,35 @@ extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* 
     if (out == nullptr || q == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
         (max_blocks_per_seq > 0 && block_table == nullptr))
         return PA_ERR_INVALID_ARG;
-    if (num_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
     if (pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
     if (pool->block_size != 16 && pool->block_size != 32) return PA_ERR_UNSUPPORTED;
-    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;
     (void)max_seqlen_k;  // the per-request lengths bound the key loop
-    const int G = num_heads / pool->num_kv_heads;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (pool->head_dim == 128)
-        return dispatch_prefill_group<128>(G, pool, out, q, batch, num_heads, cu_seqlens_q,
-                                           cu_seqlens_k, max_seqlen_q, block_table,
-                                           max_blocks_per_seq, softmax_scale, causal != 0, s);
-    if (pool->head_dim == 64)
-        return dispatch_prefill_group<64>(G, pool, out, q, batch, num_heads, cu_seqlens_q,
-                                          cu_seqlens_k, max_seqlen_q, block_table,
-                                          max_blocks_per_seq, softmax_scale, causal != 0, s);
-    return PA_ERR_UNSUPPORTED;
+    // a table of width 0 (possibly null) assigns no block: every row outputs zeros, and
+    // the kernel reads no table entry because no request then has a key to load
+    const KvSource kv{true, pool->k_cache, pool->v_cache, pool->num_kv_heads, pool->num_blocks,
+                      pool->block_size, block_table, max_blocks_per_seq};
+    return prefill_impl(kv, pool->head_dim, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,
+                        max_seqlen_q, softmax_scale, causal, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int pa_prefill_varlen_contiguous(void* out, const void* q, const void* k,
+                                            const void* v, int32_t dtype, int32_t batch,
+                                            int32_t num_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, const int32_t* cu_seqlens_q,
+                                            const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                                            int32_t max_seqlen_k, float softmax_scale,
+                                            int32_t causal, void* stream) {
+    using namespace pa;
+    if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seqlen_q < 0 ||
+        max_seqlen_k < 0)
+        return PA_ERR_INVALID_ARG;
+    if (dtype != PA_BF16 && dtype != PA_F32) return PA_ERR_INVALID_ARG;
+    if (batch == 0 || max_seqlen_q == 0) return PA_OK;
+    if (out == nullptr || q == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
+        (max_seqlen_k > 0 && (k == nullptr || v == nullptr)))
+        return PA_ERR_INVALID_ARG;
+    if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    const KvSource kv{false, k, v, num_kv_heads, 0, 0, nullptr, 0};
+    return prefill_impl(kv, head_dim, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,
+                        max_seqlen_q, softmax_scale, causal, static_cast<hipStream_t>(stream));
 }

@@ -88,6 +88,12 @@ def attend(w: W.Workload, r: DeviceRun, partition_tokens: int = 0) -> None:
                              r.table, w.scale, w.causal)
 
 
+def attend_contiguous(w: W.Workload, r: DeviceRun, k: torch.Tensor, v: torch.Tensor) -> None:
+    """The prefill over packed contiguous K/V (no block table)."""
+    pa.pa_prefill_varlen_contiguous(r.out, r.q, k, v, r.cu_q, r.cu_k, r.plan.max_q, r.plan.max_k,
+                                    w.scale, w.causal)
+
+
 def attend_append(w: W.Workload, r: DeviceRun, partition_tokens: int = 0) -> None:
     """Decode with the new tokens' K/V stored by the attention launch itself."""
     if w.kind != "decode":

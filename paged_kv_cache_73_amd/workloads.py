@@ -218,6 +218,20 @@ def chunked_prefill(seed: int = 0, batch: int = 16, q_hi: int = 512, c_hi: int =
     return prefill_workload(cached, new, seed=seed, name="chunked_prefill_r16")
 
 
+def contiguous_kv(w: Workload) -> tuple[torch.Tensor, torch.Tensor]:
+    """The workload's keys and values packed per request, without a cache: request b's
+    cached rows followed by its new rows, requests in order, ``[sum(seqlens_k), Hkv,
+    d]`` each.  (Shared-prefix workloads store a prefix once and have no such form.)"""
+    if w.groups is not None:
+        raise ValueError("a shared-prefix workload has no contiguous form")
+    ks, vs, c0, n0 = [], [], 0, 0
+    for c, n in zip(w.cached, w.new):
+        ks += [w.k_ctx[c0:c0 + c], w.k_new[n0:n0 + n]]
+        vs += [w.v_ctx[c0:c0 + c], w.v_new[n0:n0 + n]]
+        c0, n0 = c0 + c, n0 + n
+    return torch.cat(ks).contiguous(), torch.cat(vs).contiguous()
+
+
 # --------------------------------------------------------------------------------------
 # driving a block manager through a workload
 # --------------------------------------------------------------------------------------

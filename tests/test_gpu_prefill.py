@@ -147,3 +147,86 @@ def test_prefill_argument_errors():
 def test_chunked_prefill_full_size(seed):
     w = W.chunked_prefill(seed=seed)
     _run(w, requests=[0, 3, 7, 12, 15])
+
+
+# --------------------------------------------------------------------------------------
+# contiguous (non-paged) K/V
+# --------------------------------------------------------------------------------------
+
+def _contiguous_case(w, requests=None):
+    """Run the paged step and the contiguous call on the same inputs; check the
+    contiguous output against the oracle and against the paged output (bit for bit:
+    the same tiles in the same order)."""
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g)
+    k, v = W.contiguous_kv(w)
+    kd, vd = k.cuda(), v.cuda()
+    out = torch.full_like(g.out, 7.0)
+    pa.pa_prefill_varlen_contiguous(out, g.q, kd, vd, g.cu_q, g.cu_k, g.plan.max_q, g.plan.max_k,
+                                    w.scale, w.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out, g.out)
+    q = H.storage(w.q, w.dtype)
+    ks, vs = H.storage(k, w.dtype), H.storage(v, w.dtype)
+    cu_q, cu_k = g.plan.cu_q, g.plan.cu_k
+    got = H.out_f64(out)
+    for i in (range(w.batch) if requests is None else requests):
+        rq = slice(cu_q[i], cu_q[i + 1])
+        rk = slice(cu_k[i], cu_k[i + 1])
+        ref = OA.prefill_varlen_contiguous(q[rq], ks[rk], vs[rk], [0, cu_q[i + 1] - cu_q[i]],
+                                           [0, cu_k[i + 1] - cu_k[i]], w.scale, w.causal, w.dtype)
+        H.assert_close(got[rq], ref, w.dtype, f"contiguous {w.name} request {i}")
+    return out
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+@pytest.mark.parametrize("causal", [True, False])
+def test_contiguous_prefill_shapes(shape, causal):
+    hq, hkv, d, B = shape
+    rng = random.Random(hq * 3 + d + B)
+    new = [1, 5, 64, 65, 130, rng.randint(1, 200), 37, 300]
+    cached = [0, 70, 0, 3, 191, rng.randint(0, 300), 64, 0]
+    w = W.prefill_workload(cached, new, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                           block_size=B, causal=causal, seed=31)
+    _contiguous_case(w)
+
+
+def test_contiguous_prefill_edge_cases(golden):
+    # the varlen example's lengths: q [10, 3, 1], k [0, 1, 7] (request 0 has no key)
+    gx = golden("varlen_example.json")
+    hq, hkv, d = 4, 2, 64
+    gen = torch.Generator().manual_seed(32)
+    k = torch.randn((8, hkv, d), generator=gen).to(torch.bfloat16)
+    v = torch.randn((8, hkv, d), generator=gen).to(torch.bfloat16)
+    q = torch.randn((14, hq, d), generator=gen).to(torch.bfloat16)
+    cu_q, cu_k = gx["printed_cu_seq_lens_q"], gx["printed_cu_seq_lens_k"]
+    ref = OA.prefill_varlen_contiguous(H.storage(q, "bf16"), H.storage(k, "bf16"),
+                                       H.storage(v, "bf16"), cu_q, cu_k, 0.3, True, "bf16")
+    out = torch.full((14, hq, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    tq = torch.tensor(cu_q, dtype=torch.int32, device="cuda")
+    tk = torch.tensor(cu_k, dtype=torch.int32, device="cuda")
+    pa.pa_prefill_varlen_contiguous(out, q.cuda(), k.cuda(), v.cuda(), tq, tk,
+                                    gx["printed_max_length_q"], gx["printed_max_length_k"], 0.3, True)
+    torch.cuda.synchronize()
+    got = H.out_f64(out)
+    H.assert_close(got, ref, "bf16", "varlen example, contiguous")
+    assert not got[:12].any() and got[12].any() and got[13].any()
+    # batch 0 and max_seqlen_q 0 are no-ops; f32 is unsupported; bad scale is an error
+    out.fill_(7.0)
+    pa.pa_prefill_varlen_contiguous(out[:0], q[:0].cuda(), k.cuda(), v.cuda(), tq[:1], tk[:1], 0, 0,
+                                    0.3, True)
+    pa.pa_prefill_varlen_contiguous(out, q.cuda(), k.cuda(), v.cuda(), tq, tk, 0, 7, 0.3, True)
+    torch.cuda.synchronize()
+    assert bool((out.float() == 7.0).all())
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_prefill_varlen_contiguous(out.float(), q.float().cuda(), k.float().cuda(),
+                                        v.float().cuda(), tq, tk, 10, 7, 0.3, True)
+    assert e.value.code == -2
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_prefill_varlen_contiguous(out, q.cuda(), k.cuda(), v.cuda(), tq, tk, 10, 7, 0.0, True)
+    assert e.value.code == -1
+
+
+def test_contiguous_prefill_full_size():
+    w = W.chunked_prefill(seed=2)
+    _contiguous_case(w, requests=[0, 5, 11, 15])

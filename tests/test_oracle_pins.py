@@ -394,6 +394,55 @@ def test_prefill_rows_without_keys_are_zero(golden):
     assert np.any(out[13])
 
 
+def _random_contiguous(seed, q_lens, k_lens, hq, hkv, d):
+    npr = np.random.default_rng(seed)
+    k = npr.normal(size=(sum(k_lens), hkv, d)).astype(np.float32)
+    v = npr.normal(size=(sum(k_lens), hkv, d)).astype(np.float32)
+    q = npr.normal(size=(sum(q_lens), hq, d)).astype(np.float32)
+    return q, k, v, K.cu_seqlens(q_lens)[0], K.cu_seqlens(k_lens)[0]
+
+
+def check_contiguous_prefill(seed=10):
+    # nothing cached: torch's causal / full SDPA per request
+    lens = [7, 1, 12, 0, 5]
+    q, k, v, cu_q, cu_k = _random_contiguous(seed, lens, lens, 6, 3, 8)
+    for causal in (True, False):
+        out = A.prefill_varlen_contiguous(q, k, v, cu_q, cu_k, 0.3, causal, "f32")
+        for i in range(len(lens)):
+            if not lens[i]:
+                continue
+            rq, rk = slice(cu_q[i], cu_q[i + 1]), slice(cu_k[i], cu_k[i + 1])
+            ref = _sdpa(_f32(q[rq]), _f32(k[rk]), _f32(v[rk]), 0.3, causal=causal, group=2)
+            assert np.allclose(out[rq], ref, atol=1e-12), (i, causal)
+    # a cached prefix (k_len > q_len): the last rows of the one-shot causal prefill
+    n = 23
+    q, k, v, _, _ = _random_contiguous(seed + 1, [n], [n], 4, 2, 8)
+    full = A.prefill_varlen_contiguous(q, k, v, [0, n], [0, n], 0.5, True, "f32")
+    for cut in (1, 9, 22):
+        part = A.prefill_varlen_contiguous(q[cut:], k, v, [0, n - cut], [0, n], 0.5, True, "f32")
+        assert np.allclose(part, full[cut:], atol=1e-12), cut
+    # packed behind another request: the same rows
+    k2 = np.concatenate([k[:4], k])
+    v2 = np.concatenate([v[:4], v])
+    both = A.prefill_varlen_contiguous(np.concatenate([q[:3], q[5:]]), k2, v2, [0, 3, 3 + n - 5],
+                                       [0, 4, 4 + n], 0.5, True, "f32")
+    assert np.allclose(both[3:], full[5:], atol=1e-12)
+
+
+def test_contiguous_prefill_pins():
+    check_contiguous_prefill()
+
+
+def test_contiguous_prefill_equals_paged_prefill():
+    q_lens, k_lens = [5, 1, 17, 3], [9, 30, 17, 3]
+    q, kp, vp, table, cu_q, cu_k, dk, dv = _random_prefill(12, q_lens, k_lens, 4, 2, 8, 4)
+    k, v = np.concatenate(dk).astype(np.float32), np.concatenate(dv).astype(np.float32)
+    for causal in (True, False):
+        paged = A.prefill_varlen(q, kp, vp, cu_q, cu_k, table, 0.45, causal, "f32")
+        contig = A.prefill_varlen_contiguous(q, k, v, cu_q, cu_k, 0.45, causal, "f32")
+        assert np.array_equal(paged, contig)
+
+
 # --------------------------------------------------------------------------------------
 # block manager and sizing
 # --------------------------------------------------------------------------------------
@@ -593,6 +642,34 @@ def test_planted_mistakes_are_caught(monkeypatch, golden):
                                                       _f32(vv[:, h // g]), scale)
         return out
     _caught(monkeypatch, A, "prefill_varlen", top_left, check_chunked_prefill_equals_one_shot)
+    # contiguous prefill: (a) keys sliced at the query offsets, (b) causal limit off by
+    # one (a row does not see its own key)
+    def contiguous_variant(start, visible):
+        def run(q, k, v, cu_q, cu_k, scale, causal, dtype):
+            out = np.zeros(q.shape, dtype=np.float64)
+            g = q.shape[1] // k.shape[1]
+            for i in range(len(cu_q) - 1):
+                ql, kl = cu_q[i + 1] - cu_q[i], cu_k[i + 1] - cu_k[i]
+                k0 = start(cu_q, cu_k, i)
+                for t in range(ql):
+                    nv = visible(ql, kl, t) if causal else kl
+                    for h in range(q.shape[1]):
+                        out[cu_q[i] + t, h] = orig_attend(
+                            _f32(q[cu_q[i] + t, h]), _f32(k[k0:k0 + nv, h // g]),
+                            _f32(v[k0:k0 + nv, h // g]), scale)
+            return out
+        return run
+    good_visible = lambda ql, kl, t: min(max(kl - ql + t + 1, 0), kl)
+    _caught(monkeypatch, A, "prefill_varlen_contiguous",
+            contiguous_variant(lambda cq, ck, i: cq[i], good_visible), check_contiguous_prefill)
+    _caught(monkeypatch, A, "prefill_varlen_contiguous",
+            contiguous_variant(lambda cq, ck, i: ck[i], lambda ql, kl, t: min(max(kl - ql + t, 0), kl)),
+            check_contiguous_prefill)
+    # (the correct variant passes, so the two above fail for their mistake alone)
+    with monkeypatch.context() as m:
+        m.setattr(A, "prefill_varlen_contiguous",
+                  contiguous_variant(lambda cq, ck, i: ck[i], good_visible))
+        check_contiguous_prefill()
     # the freed block is appended at the bottom of the free stack
     # the prefix hash ignores the chaining
     with monkeypatch.context() as m:
