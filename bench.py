@@ -246,6 +246,26 @@ def main() -> int:
                  "launch_us_mean": 1e3 * sum(fms) / len(fms),
                  "launch_us_median": 1e3 * fms[len(fms) // 2]}
 
+    # the same prefill over contiguous K/V (no block table): the cost of paging
+    contiguous = None
+    if w.kind == "prefill" and w.groups is None:
+        from paged_kv_cache_73_amd import workloads as W
+        kc, vc = (t.to(dev) for t in W.contiguous_kv(w))
+        for _ in range(args.warmup):
+            R.attend_contiguous(w, r, kc, vc)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in cev:
+            a.record(stream)
+            R.attend_contiguous(w, r, kc, vc)
+            b.record(stream)
+        torch.cuda.synchronize()
+        cms = sorted(a.elapsed_time(b) for a, b in cev)
+        contiguous = {"launch_us_mean": 1e3 * sum(cms) / len(cms),
+                      "launch_us_median": 1e3 * cms[len(cms) // 2]}
+        del kc, vc
+
     plan = r.plan
     kernel_src = os.path.join(ROOT, "paged_kv_cache_73_amd", "csrc",
                               "decode.hip" if w.kind == "decode" else "prefill.hip")
@@ -290,7 +310,10 @@ def main() -> int:
                 "traffic": load_traffic(kernel_src, w.name), "kernel": "pa_prefill_varlen",
                 "algorithmic_flops_per_launch": fl, "launch_us_mean": attn_mean_ms * 1e3,
                 "launch_us_median": attn_median_ms * 1e3,
-                "cold_launch_us_median": None if cold_median_ms is None else cold_median_ms * 1e3}
+                "cold_launch_us_median": None if cold_median_ms is None else cold_median_ms * 1e3,
+                "contiguous_kv": contiguous}
+        if contiguous:
+            contiguous["achieved"] = fl / (contiguous["launch_us_mean"] * 1e-6) / 1e12
     line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                  "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
                  "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",

@@ -44,6 +44,7 @@ constexpr int kPrefillRows = 128;   // rows per workgroup (4 waves x 32)
 constexpr int kPrefillKeys = 64;    // keys per tile
 constexpr int kPrefillThreads = 256;
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X
+constexpr float kRescaleSlack = 8.f; // weights stay below 2^8 between rescales
 
 template <int D, int G, int BS>  // BS = 0: contiguous K/V
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
@@ -69,6 +70,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // on the transposing writes.
     constexpr int PITCH_T = BN + 2;
     __shared__ __align__(16) uint16_t k_lds[BN * PITCH];
+    constexpr int SORT_MAX = BN * PITCH / 2;  // int32 key counts that fit in k_lds
     __shared__ __align__(16) uint16_t v_lds[D * PITCH_T];
 
     // Workgroups are handed to the 8 XCDs round-robin (id L runs on XCD L % 8).  All
@@ -80,7 +82,32 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int group = (slot / n_qtiles) * kXcds + L % kXcds;
     if (group >= n_groups) return;  // grid padding
     const int hkv = group % num_kv_heads;
-    const int req = group / num_kv_heads;
+    const int tid = threadIdx.x;
+    // Groups are taken in order of decreasing key count (longest-first scheduling): the
+    // request of rank r in that order is the one with r requests ahead of it (longer,
+    // or as long and earlier in the batch).  Every workgroup derives the same order
+    // from cu_k; the key counts are staged in the K tile's LDS, which the loop below
+    // overwrites only after a barrier.
+    const int batch = n_groups / num_kv_heads;
+    const int rank = group / num_kv_heads;
+    int req = rank;
+    if (batch > 1 && batch <= SORT_MAX) {  // larger batches keep their own order
+        __shared__ int32_t found;
+        int32_t* klen = reinterpret_cast<int32_t*>(k_lds);
+        for (int j = tid; j < batch; j += kPrefillThreads) klen[j] = cu_k[j + 1] - cu_k[j];
+        __syncthreads();
+        for (int j = tid; j < batch; j += kPrefillThreads) {
+            const int kj = klen[j];
+            int ahead = 0;
+            for (int i = 0; i < batch; ++i) {
+                const int ki = klen[i];
+                ahead += (ki > kj) | ((ki == kj) & (i < j));
+            }
+            if (ahead == rank) found = j;
+        }
+        __syncthreads();
+        req = found;
+    }
     const int q0 = cu_q[req];
     const int q_len = cu_q[req + 1] - q0;
     // later query tiles see more keys under the causal mask: start them first
@@ -93,7 +120,6 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int kv_end = causal ? min(k_len, cached + tok_last + 1) : k_len;
     const int n_tiles = (kv_end > 0 && (!kPaged || num_blocks > 0)) ? (kv_end + BN - 1) / BN : 0;
 
-    const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int w = tid / kWave;
     const int h = lane / 32;      // which 8-wide half of a 16-wide k-step this lane feeds
@@ -277,7 +303,11 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
             for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[kb][x]);
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * qscale;
-        const float m_new = fmaxf(m, mx);
+        // The reference max moves only when the tile's max exceeds it by more than
+        // kRescaleSlack (base 2): the quotient sum(e^(s-m) v) / sum(e^(s-m)) does not depend
+        // on m, and a stale m keeps every weight below 2^kRescaleSlack, so O and l are
+        // rescaled in few tiles instead of nearly every one.
+        const float m_new = mx > m + kRescaleSlack ? mx : m;
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float corr = __builtin_amdgcn_exp2f(m - m_use);
         float psum = 0.f;

@@ -230,3 +230,15 @@ def test_contiguous_prefill_edge_cases(golden):
 def test_contiguous_prefill_full_size():
     w = W.chunked_prefill(seed=2)
     _contiguous_case(w, requests=[0, 5, 11, 15])
+
+
+@pytest.mark.parametrize("batch", [300, 2400])
+def test_prefill_many_requests(batch):
+    # many short requests: the longest-first order covers batches up to its limit (2304
+    # requests at d = 64) and larger ones keep the batch order; both give the same rows
+    rng = random.Random(batch)
+    new = [rng.randint(1, 3) for _ in range(batch)]
+    cached = [rng.randint(0, 40) for _ in range(batch)]
+    w = W.prefill_workload(cached, new, num_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                           seed=33)
+    _run(w, requests=list(range(0, batch, 7)))
