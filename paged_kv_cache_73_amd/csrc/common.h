@@ -16,6 +16,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 // half of a binary32, which is exact.
 struct bf16_t { uint16_t bits; };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw buffer descriptor on CDNA (32-bit data format, no swizzle).  A raw
+// buffer load whose offset is at or past the descriptor's byte count returns zeros.
+constexpr int32_t kBufferDword3 = 0x00020000;
+
+__device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
 template <typename T> struct Storage;
 template <> struct Storage<float> { static constexpr int kBytes = 4; };
 template <> struct Storage<bf16_t> { static constexpr int kBytes = 2; };

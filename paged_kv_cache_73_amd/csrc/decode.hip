@@ -50,14 +50,8 @@
 
 namespace pa {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Word 3 of a raw buffer descriptor on CDNA (32-bit data format, no swizzle).
-constexpr int32_t kBufferDword3 = 0x00020000;
 // Cache policy of the K/V page loads: non-temporal (the pages are streamed once).
 constexpr int32_t kLoadPolicy = PA_DECODE_NT ? 2 : 0;
-
-__device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
 template <typename T, int D, int BS>
 struct PageShape {

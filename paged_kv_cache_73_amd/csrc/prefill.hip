@@ -19,9 +19,11 @@
 //   l holds 16 scores of query row l%32 (the other 16 of the 32-key block sit in lane
 //   l^32).  The softmax is therefore lane-local apart from one exchange for the row max.
 //   O^T += V^T P^T then takes P straight from the S^T accumulators (the key order inside
-//   a 16-key step is permuted identically on both operands) and V^T from LDS, where V
-//   is stored transposed by the loader (a lane pair swaps halves of two keys' rows).
-// * The next tile's K/V are loaded into registers while the current tile is computed.
+//   a 16-key step is permuted identically on both operands) and V^T from LDS, where the
+//   loader stores V transposed, each 16-key group in that same permuted order so that
+//   one operand is 16 contiguous bytes.
+// * Each wave stages a 16-key slice of every tile: one page, whose address is a scalar.
+//   The next tile's K/V are loaded into registers while the current tile is computed.
 // * Masking selects: keys past the request, beyond the causal limit or in a block whose
 //   id is outside [0, num_blocks) are set to -inf before the exponent; their K/V are
 //   loaded as zeros (never from the pool), so no NaN can enter the products.
@@ -61,14 +63,16 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     constexpr int DB = D / 32;                  // 32-wide blocks of the head dim in O^T
     constexpr int PITCH = D + 8;                // LDS row pitch (elements); the pad spreads banks
     constexpr int CHUNKS = D / 8;               // 16-byte pieces per K/V row
-    constexpr int PIECES = BN * CHUNKS;         // pieces per tile (per K or V)
-    constexpr int PER_THREAD = PIECES / kPrefillThreads;
-    static_assert(PIECES % kPrefillThreads == 0, "tile split");
+    constexpr int WAVE_KEYS = BN / 4;           // keys of a tile staged by each wave
+    constexpr int KPT = WAVE_KEYS * CHUNKS / kWave;  // keys per loader thread: 4 (d 128), 2 (d 64)
+    constexpr int GPW = kWave / CHUNKS;         // key groups per wave
+    static_assert(KPT == 2 || KPT == 4, "loader split");
+    static_assert(PBS % WAVE_KEYS == 0, "a wave's keys lie in one page");
 
     // V is stored transposed (V^T[d][key]) so that an O^T operand (8 keys of one dim) is
-    // two 8-byte reads.  Pitch BN + 2: 4-byte aligned rows, 2-way bank conflicts at most
-    // on the transposing writes.
-    constexpr int PITCH_T = BN + 2;
+    // two 8-byte reads.  Pitch BN + 4: 8-byte aligned rows; the reads of 16 consecutive
+    // rows then cover all banks once, the loader's writes conflict 2-way at most.
+    constexpr int PITCH_T = BN + 4;
     __shared__ __align__(16) uint16_t k_lds[BN * PITCH];
     constexpr int SORT_MAX = BN * PITCH / 2;  // int32 key counts that fit in k_lds
     __shared__ __align__(16) uint16_t v_lds[D * PITCH_T];
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             if (ahead == rank) found = j;
         }
         __syncthreads();
-        req = found;
+        req = __builtin_amdgcn_readfirstlane(found);  // uniform: keeps the addressing scalar
     }
     const int q0 = cu_q[req];
     const int q_len = cu_q[req + 1] - q0;
@@ -121,12 +125,8 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int n_tiles = (kv_end > 0 && (!kPaged || num_blocks > 0)) ? (kv_end + BN - 1) / BN : 0;
 
     const int lane = tid % kWave;
-    const int w = tid / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave index, kept in a scalar
     const int h = lane / 32;      // which 8-wide half of a 16-wide k-step this lane feeds
-    // Loader lanes lane and lane^CHUNKS hold keys 2k and 2k+1 of the same 8 dims.
-    const int par = (lane / CHUNKS) & 1;
-    const uint32_t sel_lo = par ? 0x01000504u : 0x05040100u;  // byte selectors: (even, odd) key
-    const uint32_t sel_hi = par ? 0x03020706u : 0x07060302u;  // low / high halves
     const int r = lane % 32;
     const int row = w * 32 + r;   // row of the workgroup this lane owns
     const int tok = tok0 + row / G;
@@ -160,51 +160,33 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 
     const int32_t* table_row = kPaged ? block_table + static_cast<int64_t>(req) * max_blocks : nullptr;
     const int64_t key_base = kPaged ? 0 : cu_k[req];  // first packed row of the request (contiguous)
-    const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * D * 2;  // bytes per slot
+    const int32_t row_stride = num_kv_heads * D * 2;  // bytes per slot
 
-    // Block ids of this thread's pieces are loaded one tile before the K/V they address,
-    // so a tile's loads never wait on a table lookup.
-    int32_t ids[PER_THREAD];
-    auto fetch_ids = [&](int t) {
-        const int j0 = t * BN;
+    // Loader.  Wave w stages keys [16w, 16w+16) of every tile; they lie in one page, so
+    // the page's address is a scalar and each thread's offsets inside it never change.
+    // Thread (c, g) of the wave loads chunk c (8 dims) of the KPT consecutive keys
+    // g*KPT .. g*KPT+KPT-1, which lets it transpose V on its own: for every dim, the
+    // KPT values are adjacent in a V^T row.  A buffer descriptor bounded to the wave's
+    // valid keys makes every other load return zeros (keys past kv_end, and the whole
+    // slice of a block id outside the pool), so nothing masked can be NaN.
+    const int lc = lane / GPW;            // chunk of the row
+    const int lg = lane % GPW;            // key group inside the wave's slice
+    int32_t voff[KPT];
 #pragma unroll
-        for (int u = 0; u < PER_THREAD; ++u) {
-            const int j = j0 + (tid + u * kPrefillThreads) / CHUNKS;
-            ids[u] = kPaged ? table_row[min(j, kv_end - 1) / PBS] : 0;
-        }
-    };
-    // global -> registers for one tile, without branches: a piece that must not be read
-    // (past the end, or an id outside the pool) loads from the pool's first row and is
-    // replaced by zeros.
-    uint4 kr[PER_THREAD], vr[PER_THREAD];
-    bool ldr[PER_THREAD];
-    auto fetch = [&](int t) {
-        const int j0 = t * BN;
-#pragma unroll
-        for (int u = 0; u < PER_THREAD; ++u) {
-            const int p = tid + u * kPrefillThreads;
-            const int j = j0 + p / CHUNKS;
-            const int32_t id = ids[u];
-            const bool ok = j < kv_end &&
-                            (!kPaged || static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks));
-            const int64_t key_row = kPaged ? static_cast<int64_t>(id) * PBS + j % PBS : key_base + j;
-            const int64_t off = ok ? key_row * row_stride + static_cast<int64_t>(hkv) * D * 2 +
-                                         (p % CHUNKS) * 16
-                                   : 0;
-            // consumed (and zeroed when !ok) only when stored to LDS in the next iteration,
-            // so the loads stay in flight while the current tile is computed
-            kr[u] = *reinterpret_cast<const uint4*>(k_cache + off);
-            vr[u] = *reinterpret_cast<const uint4*>(v_cache + off);
-            ldr[u] = ok;
-        }
-    };
+    for (int u = 0; u < KPT; ++u) voff[u] = (lg * KPT + u) * row_stride + lc * 16;
+    const int64_t head_off = static_cast<int64_t>(hkv) * D * 2;
 
-    // Validity of the tile's pages (uniform): bit i set when page i of the tile is either
-    // past kv_end or holds a block id inside the pool.
+    // Block ids and page validity are scalars read one tile ahead of the loads that use
+    // them (no arrays: the addressing must stay in scalar registers).
     constexpr int PAGES = BN / PBS;
-    auto tile_pages_ok = [&](int t) {
+    auto wave_id = [&](int t) -> int32_t {  // block id of this wave's slice of tile t
+        const int kw0 = t * BN + WAVE_KEYS * w;
+        return (kPaged && kw0 < kv_end) ? table_row[kw0 / PBS] : 0;
+    };
+    // bit i set when page i of tile t is either past kv_end or holds a block id inside the pool
+    auto pages_ok = [&](int t) -> uint32_t {
+        if constexpr (!kPaged) return 1u;
         uint32_t bits = 0;
-        if (!kPaged) return 1u;
 #pragma unroll
         for (int i = 0; i < PAGES; ++i) {
             const int jp = t * BN + i * PBS;
@@ -213,49 +195,74 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         }
         return bits;
     };
-    uint32_t ok_next = 0;
+    uint4 kr[KPT], vr[KPT];
+    auto fetch = [&](int t, int32_t id) {
+        const int kw0 = t * BN + WAVE_KEYS * w;            // first key of this wave's slice
+        const int nvalid = min(max(kv_end - kw0, 0), WAVE_KEYS);
+        bool ok = nvalid > 0;
+        int64_t base;
+        if constexpr (kPaged) {
+            ok = ok && static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks);
+            base = (static_cast<int64_t>(id) * PBS + kw0 % PBS) * row_stride + head_off;
+        } else {
+            base = (key_base + kw0) * row_stride + head_off;
+        }
+        if (!ok) base = 0;
+        // (readfirstlane: a value the compiler forms on the vector unit would otherwise turn
+        // each load into a loop over lanes)
+        const int32_t bytes = __builtin_amdgcn_readfirstlane(ok ? nvalid * row_stride : 0);
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(k_cache + base), 0, bytes, kBufferDword3);
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(v_cache + base), 0, bytes, kBufferDword3);
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            kr[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(krs, voff[u], 0, 0));
+            vr[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(vrs, voff[u], 0, 0));
+        }
+    };
+
+    int32_t id_next = 0;
+    uint32_t ok_cur = 0, ok_next = 0;
     if (n_tiles > 0) {
-        fetch_ids(0);
-        fetch(0);
-        ok_next = tile_pages_ok(0);
-        if (n_tiles > 1) fetch_ids(1);
+        fetch(0, wave_id(0));
+        ok_cur = pages_ok(0);
+        if (n_tiles > 1) id_next = wave_id(1), ok_next = pages_ok(1);
     }
     for (int t = 0; t < n_tiles; ++t) {
         const int j0 = t * BN;
         __syncthreads();  // the previous tile is no longer read
-        const uint32_t page_ok = ok_next;
+        const uint32_t page_ok = ok_cur;
         const bool tile_ok = page_ok == (1u << PAGES) - 1;
+        {
+            // K rows as they are; V^T rows: for dim 8lc + e, this thread's KPT keys, at the
+            // position of their 4-key quad q in the group's order q0 q2 q1 q3
+            const int key0 = WAVE_KEYS * w + lg * KPT;
 #pragma unroll
-        for (int u = 0; u < PER_THREAD; ++u) {
-            const int p = tid + u * kPrefillThreads;
-            const int key = p / CHUNKS;
-            const int chunk = p % CHUNKS;
-            const uint4 z = make_uint4(0, 0, 0, 0);
-            if (!ldr[u]) kr[u] = z, vr[u] = z;
-            *reinterpret_cast<uint4*>(&k_lds[key * PITCH + chunk * 8]) = kr[u];
-            {
-                // transpose through a lane pair: the even-key lane writes dims 0-3 of both
-                // keys, the odd-key lane dims 4-7, one 4-byte (two-key) word per dim
-                const uint32_t d0 = vr[u].x, d1 = vr[u].y, d2 = vr[u].z, d3 = vr[u].w;
-                const uint32_t send0 = par ? d0 : d2, send1 = par ? d1 : d3;
-                const uint32_t own0 = par ? d2 : d0, own1 = par ? d3 : d1;
-                const uint32_t rec0 = __shfl_xor(send0, CHUNKS), rec1 = __shfl_xor(send1, CHUNKS);
-                const int rb = chunk * 8 + 4 * par;
-                uint32_t* vt = reinterpret_cast<uint32_t*>(v_lds);
-                const int col = key / 2;
-                vt[((rb + 0) * PITCH_T) / 2 + col] = __builtin_amdgcn_perm(rec0, own0, sel_lo);
-                vt[((rb + 1) * PITCH_T) / 2 + col] = __builtin_amdgcn_perm(rec0, own0, sel_hi);
-                vt[((rb + 2) * PITCH_T) / 2 + col] = __builtin_amdgcn_perm(rec1, own1, sel_lo);
-                vt[((rb + 3) * PITCH_T) / 2 + col] = __builtin_amdgcn_perm(rec1, own1, sel_hi);
+            for (int u = 0; u < KPT; ++u)
+                *reinterpret_cast<uint4*>(&k_lds[(key0 + u) * PITCH + lc * 8]) = kr[u];
+            const int quad = (lg * KPT) / 4;
+            const int col = WAVE_KEYS * w + (quad & 1) * 8 + (quad >> 1) * 4 + (lg * KPT) % 4;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+                const int i = e / 2;
+                uint32_t* dst = reinterpret_cast<uint32_t*>(&v_lds[(lc * 8 + e) * PITCH_T + col]);
+                const uint32_t p01 = __builtin_amdgcn_perm(word(vr[1], i), word(vr[0], i), sel);
+                if constexpr (KPT == 4) {
+                    const uint32_t p23 = __builtin_amdgcn_perm(word(vr[3], i), word(vr[2], i), sel);
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(p01, p23);
+                } else {
+                    *dst = p01;
+                }
             }
         }
         __syncthreads();
         if (t + 1 < n_tiles) {  // in flight while this tile is computed
-            fetch(t + 1);
-            ok_next = tile_pages_ok(t + 1);
-            if (t + 2 < n_tiles) fetch_ids(t + 2);
+            fetch(t + 1, id_next);
+            ok_cur = ok_next;
+            if (t + 2 < n_tiles) id_next = wave_id(t + 2), ok_next = pages_ok(t + 2);
         }
-
         if (j0 > wave_hi) continue;  // no row of this wave sees any key of the tile
 
         // S^T blocks: keys j0 + 32kb + (8i + 4h + jj), query row = this lane's row
@@ -330,13 +337,14 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                 for (int x = 0; x < 16; ++x) acc[db][x] *= corr;
         }
 
-        // O^T += V^T P^T: A = V^T rows d = 32db + r, keys 16ks + 4h + (e%4) + 8(e/4)
+        // O^T += V^T P^T: A = V^T rows d = 32db + r, keys 16ks + 4h + (e%4) + 8(e/4),
+        // stored contiguously at 16ks + 8h (quads h and 2 + h)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const uint2 lo = *reinterpret_cast<const uint2*>(&v_lds[(32 * db + r) * PITCH_T + 16 * ks + 4 * h]);
-                const uint2 hi = *reinterpret_cast<const uint2*>(&v_lds[(32 * db + r) * PITCH_T + 16 * ks + 8 + 4 * h]);
+                const uint2 lo = *reinterpret_cast<const uint2*>(&v_lds[(32 * db + r) * PITCH_T + 16 * ks + 8 * h]);
+                const uint2 hi = *reinterpret_cast<const uint2*>(&v_lds[(32 * db + r) * PITCH_T + 16 * ks + 8 * h + 4]);
                 const u16x8_t a = __builtin_bit_cast(u16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[ks], acc[db], 0, 0, 0);
             }
