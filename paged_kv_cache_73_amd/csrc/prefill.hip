@@ -42,11 +42,42 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 
+// LDS buffers for K/V tiles: 2 stages the next tile while the current one is read.
+#ifndef PA_PREFILL_LDS_BUFFERS
+#define PA_PREFILL_LDS_BUFFERS 2
+#endif
+// Raise the wave's priority while it issues matrix products (1) or not (0).
+#ifndef PA_PREFILL_SETPRIO
+#define PA_PREFILL_SETPRIO 1
+#endif
+// MFMA operands read from LDS ahead of the product that uses them.
+#ifndef PA_PREFILL_LDS_AHEAD
+#define PA_PREFILL_LDS_AHEAD 4
+#endif
+// Padding (elements) of a V^T row in LDS.
+#ifndef PA_PREFILL_VT_PAD
+#define PA_PREFILL_VT_PAD 4
+#endif
+
 constexpr int kPrefillRows = 128;   // rows per workgroup (4 waves x 32)
 constexpr int kPrefillKeys = 64;    // keys per tile
 constexpr int kPrefillThreads = 256;
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X
 constexpr float kRescaleSlack = 8.f; // weights stay below 2^8 between rescales
+
+// Instruction order for a run of N products whose operands come from LDS: AHEAD reads
+// first, then each product followed by the next read, so that AHEAD reads stay in
+// flight (the scheduler otherwise moves every read next to its product).
+template <int N, int AHEAD>
+__device__ __forceinline__ void pipeline_order() {
+    constexpr int kLdsRead = 0x100, kMfma = 0x008;
+    __builtin_amdgcn_sched_group_barrier(kLdsRead, AHEAD, 0);
+#pragma unroll
+    for (int o = 0; o < N; ++o) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        if (o + AHEAD < N) __builtin_amdgcn_sched_group_barrier(kLdsRead, 1, 0);
+    }
+}
 
 template <int D, int G, int BS>  // BS = 0: contiguous K/V
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
@@ -72,10 +103,13 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // V is stored transposed (V^T[d][key]) so that an O^T operand (8 keys of one dim) is
     // two 8-byte reads.  Pitch BN + 4: 8-byte aligned rows; the reads of 16 consecutive
     // rows then cover all banks once, the loader's writes conflict 2-way at most.
-    constexpr int PITCH_T = BN + 4;
-    __shared__ __align__(16) uint16_t k_lds[BN * PITCH];
+    constexpr int PITCH_T = BN + PA_PREFILL_VT_PAD;
+    constexpr int LDS_AHEAD = PA_PREFILL_LDS_AHEAD;  // MFMA operands read ahead of use
+    constexpr int NBUF = PA_PREFILL_LDS_BUFFERS;  // 2: the next tile is staged while this one is read
+    __shared__ __align__(16) uint16_t k_lds_all[NBUF][BN * PITCH];
+    __shared__ __align__(16) uint16_t v_lds_all[NBUF][D * PITCH_T];
+    uint16_t* const k_lds = k_lds_all[0];
     constexpr int SORT_MAX = BN * PITCH / 2;  // int32 key counts that fit in k_lds
-    __shared__ __align__(16) uint16_t v_lds[D * PITCH_T];
 
     // Workgroups are handed to the 8 XCDs round-robin (id L runs on XCD L % 8).  All
     // query tiles of one (request, KV head) group read the same K/V pages, so they are
@@ -176,24 +210,44 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     for (int u = 0; u < KPT; ++u) voff[u] = (lg * KPT + u) * row_stride + lc * 16;
     const int64_t head_off = static_cast<int64_t>(hkv) * D * 2;
 
-    // Block ids and page validity are scalars read one tile ahead of the loads that use
-    // them (no arrays: the addressing must stay in scalar registers).
+    // Block ids of a tile's pages come from one vector load (all lanes read the same
+    // words), issued a tile ahead together with the K/V loads so the wait that precedes
+    // the LDS stores covers it; scalar loads would instead hold up the next LDS wait,
+    // which shares their counter.  The words are moved to scalar registers when used.
     constexpr int PAGES = BN / PBS;
-    auto wave_id = [&](int t) -> int32_t {  // block id of this wave's slice of tile t
-        const int kw0 = t * BN + WAVE_KEYS * w;
-        return (kPaged && kw0 < kv_end) ? table_row[kw0 / PBS] : 0;
-    };
-    // bit i set when page i of tile t is either past kv_end or holds a block id inside the pool
-    auto pages_ok = [&](int t) -> uint32_t {
-        if constexpr (!kPaged) return 1u;
-        uint32_t bits = 0;
-#pragma unroll
-        for (int i = 0; i < PAGES; ++i) {
-            const int jp = t * BN + i * PBS;
-            const int32_t id = jp < kv_end ? table_row[jp / PBS] : 0;
-            bits |= (static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks) ? 1u : 0u) << i;
+    const __amdgpu_buffer_rsrc_t table_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(kPaged ? table_row : cu_k), 0, kPaged ? max_blocks * 4 : 0,
+        kBufferDword3);
+    auto load_ids = [&](int t) -> u32x4 {  // ids of tile t's pages; zero past the table
+        const int off = t * PAGES * 4;
+        if constexpr (!kPaged) {
+            return u32x4{0, 0, 0, 0};
+        } else if constexpr (PAGES == 4) {
+            return __builtin_amdgcn_raw_buffer_load_b128(table_rsrc, off, 0, 0);
+        } else if constexpr (PAGES == 2) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b64(table_rsrc, off, 0, 0);
+            return u32x4{x[0], x[1], 0, 0};
+        } else {
+            return u32x4{__builtin_amdgcn_raw_buffer_load_b32(table_rsrc, off, 0, 0), 0, 0, 0};
         }
-        return bits;
+    };
+    struct TileIds {
+        uint32_t bits;  // bit i: page i is past kv_end or holds a block id inside the pool
+        int32_t wave;   // block id of this wave's slice
+    };
+    auto scalar_ids = [&](int t, const u32x4& v) {
+        TileIds r{1u, 0};
+        if constexpr (kPaged) {
+            r.bits = 0;
+#pragma unroll
+            for (int i = 0; i < PAGES; ++i) {
+                const int32_t id = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(v[i]));
+                const bool past = t * BN + i * PBS >= kv_end;
+                r.bits |= (past || static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks) ? 1u : 0u) << i;
+                if ((WAVE_KEYS * w) / PBS == i) r.wave = id;
+            }
+        }
+        return r;
     };
     uint4 kr[KPT], vr[KPT];
     auto fetch = [&](int t, int32_t id) {
@@ -222,61 +276,77 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         }
     };
 
-    int32_t id_next = 0;
-    uint32_t ok_cur = 0, ok_next = 0;
+    // ids of tile t + 1 are loaded during tile t - 1 and used during tile t
+    u32x4 ids_next = u32x4{0, 0, 0, 0};
+    uint32_t ok_cur = 0;
     if (n_tiles > 0) {
-        fetch(0, wave_id(0));
-        ok_cur = pages_ok(0);
-        if (n_tiles > 1) id_next = wave_id(1), ok_next = pages_ok(1);
+        const TileIds first = scalar_ids(0, load_ids(0));
+        fetch(0, first.wave);
+        ok_cur = first.bits;
+        if (n_tiles > 1) ids_next = load_ids(1);
     }
-    for (int t = 0; t < n_tiles; ++t) {
-        const int j0 = t * BN;
-        __syncthreads();  // the previous tile is no longer read
-        const uint32_t page_ok = ok_cur;
-        const bool tile_ok = page_ok == (1u << PAGES) - 1;
-        {
-            // K rows as they are; V^T rows: for dim 8lc + e, this thread's KPT keys, at the
-            // position of their 4-key quad q in the group's order q0 q2 q1 q3
-            const int key0 = WAVE_KEYS * w + lg * KPT;
-#pragma unroll
-            for (int u = 0; u < KPT; ++u)
-                *reinterpret_cast<uint4*>(&k_lds[(key0 + u) * PITCH + lc * 8]) = kr[u];
-            const int quad = (lg * KPT) / 4;
-            const int col = WAVE_KEYS * w + (quad & 1) * 8 + (quad >> 1) * 4 + (lg * KPT) % 4;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-                const int i = e / 2;
-                uint32_t* dst = reinterpret_cast<uint32_t*>(&v_lds[(lc * 8 + e) * PITCH_T + col]);
-                const uint32_t p01 = __builtin_amdgcn_perm(word(vr[1], i), word(vr[0], i), sel);
-                if constexpr (KPT == 4) {
-                    const uint32_t p23 = __builtin_amdgcn_perm(word(vr[3], i), word(vr[2], i), sel);
-                    *reinterpret_cast<uint2*>(dst) = make_uint2(p01, p23);
-                } else {
-                    *dst = p01;
+    // registers -> LDS buffer b for the tile whose loads are in kr / vr
+    auto stage = [&](int b) {
+            {
+                // K rows as they are; V^T rows: for dim 8lc + e, this thread's KPT keys, at the
+                // position of their 4-key quad q in the group's order q0 q2 q1 q3
+                const int key0 = WAVE_KEYS * w + lg * KPT;
+    #pragma unroll
+                for (int u = 0; u < KPT; ++u)
+                    *reinterpret_cast<uint4*>(&k_lds_all[b][(key0 + u) * PITCH + lc * 8]) = kr[u];
+                const int quad = (lg * KPT) / 4;
+                const int col = WAVE_KEYS * w + (quad & 1) * 8 + (quad >> 1) * 4 + (lg * KPT) % 4;
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+                    const int i = e / 2;
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(&v_lds_all[b][(lc * 8 + e) * PITCH_T + col]);
+                    const uint32_t p01 = __builtin_amdgcn_perm(word(vr[1], i), word(vr[0], i), sel);
+                    if constexpr (KPT == 4) {
+                        const uint32_t p23 = __builtin_amdgcn_perm(word(vr[3], i), word(vr[2], i), sel);
+                        if constexpr (PITCH_T % 4 == 0) {
+                            *reinterpret_cast<uint2*>(dst) = make_uint2(p01, p23);
+                        } else {  // rows only 4-byte aligned
+                            dst[0] = p01;
+                            dst[1] = p23;
+                        }
+                    } else {
+                        *dst = p01;
+                    }
                 }
             }
-        }
-        __syncthreads();
-        if (t + 1 < n_tiles) {  // in flight while this tile is computed
-            fetch(t + 1, id_next);
-            ok_cur = ok_next;
-            if (t + 2 < n_tiles) id_next = wave_id(t + 2), ok_next = pages_ok(t + 2);
-        }
-        if (j0 > wave_hi) continue;  // no row of this wave sees any key of the tile
+    };
+    // one tile from LDS buffer b: scores, online softmax, and the P V products
+    auto compute = [&](int t, int b, uint32_t page_ok) {
+        const int j0 = t * BN;
+        const bool tile_ok = page_ok == (1u << PAGES) - 1;
 
         // S^T blocks: keys j0 + 32kb + (8i + 4h + jj), query row = this lane's row
+        // The two 32-key blocks alternate, so consecutive products are independent, and
+        // the K operands are read LDS_AHEAD products before their use.
         f32x16_t s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int x = 0; x < 16; ++x) s[kb][x] = 0.f;
+        if constexpr (PA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        {
+            constexpr int N = 2 * KS;
+            auto read_k = [&](int o) {  // product o: k-step o / 2 of key block o % 2
+                return *reinterpret_cast<const u16x8_t*>(&k_lds_all[b][((o % 2) * 32 + r) * PITCH + (o / 2) * 16 + 8 * h]);
+            };
+            u16x8_t kbuf[LDS_AHEAD];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u16x8_t a = *reinterpret_cast<const u16x8_t*>(&k_lds[(kb * 32 + r) * PITCH + ks * 16 + 8 * h]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qf[ks], s[kb], 0, 0, 0);
+            for (int o = 0; o < LDS_AHEAD; ++o) kbuf[o] = read_k(o);
+#pragma unroll
+            for (int o = 0; o < N; ++o) {
+                const u16x8_t a = kbuf[o % LDS_AHEAD];
+                if (o + LDS_AHEAD < N) kbuf[o % LDS_AHEAD] = read_k(o + LDS_AHEAD);
+                s[o % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qf[o / 2], s[o % 2], 0, 0, 0);
             }
+            pipeline_order<N, LDS_AHEAD>();
         }
+        if constexpr (PA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
 
         // scale to base 2, mask, running max
         const bool need_mask = !tile_ok || j0 + BN - 1 > wave_lo;
@@ -339,15 +409,80 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 
         // O^T += V^T P^T: A = V^T rows d = 32db + r, keys 16ks + 4h + (e%4) + 8(e/4),
         // stored contiguously at 16ks + 8h (quads h and 2 + h)
+        // (products alternate over the DB accumulators; operands read LDS_AHEAD ahead)
+        if constexpr (PA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        {
+            constexpr int N = 4 * DB;
+            auto read_v = [&](int o) {  // product o: k-step o / DB of dim block o % DB
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                    &v_lds_all[b][(32 * (o % DB) + r) * PITCH_T + 16 * (o / DB) + 8 * h]);
+                uint2 lo, hi;
+                if constexpr (PITCH_T % 4 == 0) {
+                    lo = *reinterpret_cast<const uint2*>(src);
+                    hi = *reinterpret_cast<const uint2*>(src + 2);
+                } else {  // rows only 4-byte aligned
+                    lo = make_uint2(src[0], src[1]);
+                    hi = make_uint2(src[2], src[3]);
+                }
+                return __builtin_bit_cast(u16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            };
+            u16x8_t vbuf[LDS_AHEAD];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+            for (int o = 0; o < LDS_AHEAD; ++o) vbuf[o] = read_v(o);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const uint2 lo = *reinterpret_cast<const uint2*>(&v_lds[(32 * db + r) * PITCH_T + 16 * ks + 8 * h]);
-                const uint2 hi = *reinterpret_cast<const uint2*>(&v_lds[(32 * db + r) * PITCH_T + 16 * ks + 8 * h + 4]);
-                const u16x8_t a = __builtin_bit_cast(u16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[ks], acc[db], 0, 0, 0);
+            for (int o = 0; o < N; ++o) {
+                const u16x8_t a = vbuf[o % LDS_AHEAD];
+                if (o + LDS_AHEAD < N) vbuf[o % LDS_AHEAD] = read_v(o + LDS_AHEAD);
+                acc[o % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[o / DB], acc[o % DB], 0, 0, 0);
             }
+            pipeline_order<N, LDS_AHEAD>();
+        }
+        if constexpr (PA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    };
+
+    if constexpr (NBUF == 2) {
+        // one barrier per tile: tile t + 1 is staged into the other buffer after tile t
+        // is computed, while the loads of tile t + 2 are issued
+        uint32_t ok_pend = 0;
+        if (n_tiles > 0) {
+            __syncthreads();  // the request order staged in k_lds is no longer read
+            stage(0);
+            if (n_tiles > 1) {
+                const TileIds next = scalar_ids(1, ids_next);
+                fetch(1, next.wave);
+                ok_pend = next.bits;
+                if (n_tiles > 2) ids_next = load_ids(2);
+            }
+            __syncthreads();
+        }
+        for (int t = 0; t < n_tiles; ++t) {
+            const int b = t & 1;
+            if (t * BN <= wave_hi) compute(t, b, ok_cur);
+            if (t + 1 < n_tiles) {
+                stage(b ^ 1);
+                ok_cur = ok_pend;
+                if (t + 2 < n_tiles) {
+                    const TileIds next = scalar_ids(t + 2, ids_next);
+                    fetch(t + 2, next.wave);
+                    ok_pend = next.bits;
+                    if (t + 3 < n_tiles) ids_next = load_ids(t + 3);
+                }
+            }
+            __syncthreads();
+        }
+    } else {
+        for (int t = 0; t < n_tiles; ++t) {
+            __syncthreads();  // the previous tile is no longer read
+            const uint32_t page_ok = ok_cur;
+            stage(0);
+            __syncthreads();
+            if (t + 1 < n_tiles) {  // in flight while this tile is computed
+                const TileIds next = scalar_ids(t + 1, ids_next);
+                fetch(t + 1, next.wave);
+                ok_cur = next.bits;
+                if (t + 2 < n_tiles) ids_next = load_ids(t + 2);
+            }
+            if (t * BN <= wave_hi) compute(t, 0, page_ok);  // else no row of this wave sees the tile
         }
     }
 
