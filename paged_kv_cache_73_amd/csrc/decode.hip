@@ -83,6 +83,20 @@ __device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[E], int
     m = m_new;
 }
 
+// Packed query tokens in place of sequences (the varlen prefill run token by token):
+// "sequence" b is query token offset + blockIdx.z of the packed batch, its request is
+// the one whose [cu_q[i], cu_q[i+1]) holds it, and it attends to that request's first
+// k_len keys, or to keys j <= c + t when causal (c = k_len - q_len, t its index in the
+// request).  cu_q == nullptr: ordinary decode.
+struct TokenMap {
+    const int32_t* cu_q = nullptr;
+    const int32_t* cu_k = nullptr;
+    int32_t n_req = 0;
+    int32_t causal = 0;
+    int32_t offset = 0;
+    int32_t max_q = 0;  // tokens of a request past max_q are not computed
+};
+
 #if PA_DECODE_WAVES_PER_EU > 0
 #define PA_DECODE_ATTR __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
 #else
@@ -96,7 +110,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     const T* __restrict__ k_new, const T* __restrict__ v_new,
     T* __restrict__ out, float* __restrict__ o_part, float* __restrict__ ml_part,
     int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks, int32_t max_blocks,
-    int32_t max_parts, int32_t part_pages, float qscale) {
+    int32_t max_parts, int32_t part_pages, float qscale, TokenMap tm) {
     using S = PageShape<T, D, BS>;
     constexpr int LPR = S::kLanesPerRow;
     constexpr int RPL = S::kRowsPerLoad;
@@ -107,12 +121,30 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     const int heads_per_wg = blockDim.x / kWave;
     const int hkv = blockIdx.x * heads_per_wg + threadIdx.x / kWave;
     const int part = blockIdx.y;
-    const int b = blockIdx.z;
+    const int b = blockIdx.z + tm.offset;
     const int r0 = lane / LPR;  // first row of this lane within a load
     const int c = lane % LPR;   // 16-byte piece of the row
 
     const int32_t cap = max_blocks * BS;
-    const int32_t seqlen = min(max(seqlens[b], 0), cap);
+    int32_t n_keys;
+    int64_t row_index = b;  // block-table row
+    if (tm.cu_q != nullptr) {
+        if (b >= tm.cu_q[tm.n_req]) return;  // past the packed tokens (uniform)
+        int lo = 0, hi = tm.n_req;           // cu_q[lo] <= b < cu_q[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tm.cu_q[mid] <= b) lo = mid; else hi = mid;
+        }
+        const int32_t q_len = tm.cu_q[lo + 1] - tm.cu_q[lo];
+        const int32_t k_len = tm.cu_k[lo + 1] - tm.cu_k[lo];
+        const int32_t t = b - tm.cu_q[lo];
+        if (t >= tm.max_q) return;
+        n_keys = tm.causal ? min(k_len, k_len - q_len + t + 1) : k_len;
+        row_index = lo;
+    } else {
+        n_keys = seqlens[b];
+    }
+    const int32_t seqlen = min(max(n_keys, 0), cap);
     const int32_t part_tokens = part_pages * BS;
     const int32_t n_parts = max(1, (seqlen + part_tokens - 1) / part_tokens);
     if (part >= n_parts) return;  // uniform over the workgroup
@@ -135,7 +167,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     // Fused append (k_new != null): the current token sits at position seqlen - 1.  The
     // workgroup of the last partition stores its K/V row in the cache and, when it
     // consumes that page, takes the row from registers rather than from memory.
-    const int32_t* table_row = block_table + static_cast<int64_t>(b) * max_blocks;
+    const int32_t* table_row = block_table + row_index * max_blocks;
     const bool appending = k_new != nullptr && seqlen > 0 && part == n_parts - 1;
     const int32_t new_pos = seqlen - 1;
     uint4 nk = make_uint4(0, 0, 0, 0), nv = make_uint4(0, 0, 0, 0);
@@ -403,7 +435,8 @@ template <typename T, int D, int BS, int G>
 int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                   int32_t num_heads, const int32_t* table, int32_t max_blocks,
                   const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
-                  int32_t part_tokens, float scale, float* o_part, float* ml_part, hipStream_t stream) {
+                  int32_t part_tokens, float scale, float* o_part, float* ml_part, hipStream_t stream,
+                  const TokenMap& tm) {
     const int hkv = pool->num_kv_heads;
     int per_wg = PA_DECODE_HPW;
     while (hkv % per_wg != 0) per_wg >>= 1;
@@ -413,7 +446,7 @@ int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batc
                        static_cast<char*>(pool->v_cache), table, seqlens,
                        static_cast<const T*>(k_new), static_cast<const T*>(v_new),
                        static_cast<T*>(out), o_part, ml_part, num_heads, hkv, pool->num_blocks,
-                       max_blocks, max_parts, part_tokens / BS, scale * kLog2e);
+                       max_blocks, max_parts, part_tokens / BS, scale * kLog2e, tm);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     if (max_parts > 1) {
         hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(num_heads, batch), dim3(kWave), 0,
@@ -428,12 +461,12 @@ int dispatch_group(int G, const pa_kv_pool* pool, void* out, const void* q, int3
                    int32_t num_heads, const int32_t* table, int32_t max_blocks,
                    const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
                    int32_t part_tokens, float scale, float* o_part, float* ml_part,
-                   hipStream_t stream) {
+                   hipStream_t stream, const TokenMap& tm) {
 #define PA_DECODE_G(GG)                                                                    \
     case GG:                                                                               \
         return launch_decode<T, D, BS, GG>(pool, out, q, batch, num_heads, table, max_blocks, \
                                            seqlens, k_new, v_new, max_parts, part_tokens,    \
-                                           scale, o_part, ml_part, stream);
+                                           scale, o_part, ml_part, stream, tm);
     switch (G) {
         PA_DECODE_G(1)
         PA_DECODE_G(2)
@@ -449,13 +482,13 @@ int dispatch_shape(int G, const pa_kv_pool* pool, void* out, const void* q, int3
                    int32_t num_heads, const int32_t* table, int32_t max_blocks,
                    const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
                    int32_t part_tokens, float scale, float* o_part, float* ml_part,
-                   hipStream_t stream) {
+                   hipStream_t stream, const TokenMap& tm) {
     const int D = pool->head_dim, BS = pool->block_size;
 #define PA_DECODE_SHAPE(DD, BB)                                                             \
     if (D == DD && BS == BB)                                                                \
         return dispatch_group<T, DD, BB>(G, pool, out, q, batch, num_heads, table, max_blocks, \
                                          seqlens, k_new, v_new, max_parts, part_tokens,       \
-                                         scale, o_part, ml_part, stream);
+                                         scale, o_part, ml_part, stream, tm);
     PA_DECODE_SHAPE(64, 16)
     PA_DECODE_SHAPE(64, 32)
     PA_DECODE_SHAPE(128, 16)
@@ -525,10 +558,43 @@ int decode_impl(const pa_kv_pool* pool, void* out, const void* q, const void* k_
     if (pool->dtype == PA_BF16)
         return dispatch_shape<bf16_t>(G, pool, out, q, batch, num_heads, block_table,
                                       max_blocks_per_seq, seqlens_k, k_new, v_new, max_parts,
-                                      part_tokens, softmax_scale, o_part, ml_part, s);
+                                      part_tokens, softmax_scale, o_part, ml_part, s, TokenMap{});
     return dispatch_shape<float>(G, pool, out, q, batch, num_heads, block_table,
                                  max_blocks_per_seq, seqlens_k, k_new, v_new, max_parts,
-                                 part_tokens, softmax_scale, o_part, ml_part, s);
+                                 part_tokens, softmax_scale, o_part, ml_part, s, TokenMap{});
+}
+
+// The varlen prefill run one packed query token at a time by the decode kernel, each
+// token over its request's keys in a single partition (no workspace).  No matrix cores:
+// the path for pools the MFMA prefill does not take (fp32).  Arguments as for
+// pa_prefill_varlen, already checked by it.
+int prefill_by_token(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                     int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
+                     int32_t max_seqlen_q, const int32_t* block_table, int32_t max_blocks,
+                     float scale, int32_t causal, hipStream_t s) {
+    if (pool->num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
+    const int32_t part_tokens = std::max(max_blocks, 1) * pool->block_size;  // one partition
+    const int G = num_heads / pool->num_kv_heads;
+    const int64_t bound = static_cast<int64_t>(batch) * max_seqlen_q;  // tokens, at most
+    for (int64_t first = 0; first < bound; first += 65535) {
+        const int32_t n = static_cast<int32_t>(std::min<int64_t>(65535, bound - first));
+        TokenMap tm;
+        tm.cu_q = cu_q;
+        tm.cu_k = cu_k;
+        tm.n_req = batch;
+        tm.causal = causal != 0;
+        tm.offset = static_cast<int32_t>(first);
+        tm.max_q = max_seqlen_q;
+        const int st = pool->dtype == PA_BF16
+            ? dispatch_shape<bf16_t>(G, pool, out, q, n, num_heads, block_table, max_blocks,
+                                     nullptr, nullptr, nullptr, 1, part_tokens, scale, nullptr,
+                                     nullptr, s, tm)
+            : dispatch_shape<float>(G, pool, out, q, n, num_heads, block_table, max_blocks,
+                                    nullptr, nullptr, nullptr, 1, part_tokens, scale, nullptr,
+                                    nullptr, s, tm);
+        if (st != PA_OK) return st;
+    }
+    return PA_OK;
 }
 
 }  // namespace pa

@@ -503,6 +503,13 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         }
 }
 
+// The varlen prefill run token by token on the decode kernel (decode.hip): the path
+// for fp32 pools.
+int prefill_by_token(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                     int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
+                     int32_t max_seqlen_q, const int32_t* block_table, int32_t max_blocks,
+                     float scale, int32_t causal, hipStream_t s);
+
 // Where the keys live: a paged pool (table != null) or packed contiguous arrays.
 struct KvSource {
     bool paged;
@@ -589,8 +596,15 @@ extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* 
     if (out == nullptr || q == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
         (max_blocks_per_seq > 0 && block_table == nullptr))
         return PA_ERR_INVALID_ARG;
-    if (pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
     if (pool->block_size != 16 && pool->block_size != 32) return PA_ERR_UNSUPPORTED;
+    if (pool->dtype == PA_F32) {
+        if (num_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+        if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;
+        return prefill_by_token(pool, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,
+                                max_seqlen_q, block_table, max_blocks_per_seq, softmax_scale,
+                                causal, static_cast<hipStream_t>(stream));
+    }
+    if (pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
     (void)max_seqlen_k;  // the per-request lengths bound the key loop
     // a table of width 0 (possibly null) assigns no block: every row outputs zeros, and
     // the kernel reads no table entry because no request then has a key to load

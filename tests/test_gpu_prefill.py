@@ -134,13 +134,100 @@ def test_prefill_unassigned_block_is_masked():
 
 
 def test_prefill_argument_errors():
-    w = W.prefill_workload([4], [4], dtype="f32", num_heads=4, num_kv_heads=2, head_dim=64, seed=26)
+    w = W.prefill_workload([4], [4], num_heads=4, num_kv_heads=2, head_dim=64, seed=26)
     g = H.gpu_setup(w)
-    with pytest.raises(pa.PaError) as e:
-        pa.pa_prefill_varlen(g.pool, g.out, g.q, g.cu_q, g.cu_k, 4, 8, g.table, w.scale, True)
-    assert e.value.code == -2   # fp32 prefill is not implemented
+    with pytest.raises(pa.PaError) as e:   # the scale must be positive
+        pa.pa_prefill_varlen(g.pool, g.out, g.q, g.cu_q, g.cu_k, 4, 8, g.table, 0.0, True)
+    assert e.value.code == -1
+    with pytest.raises(pa.PaError) as e:   # Hq not a multiple of Hkv
+        pa.pa_prefill_varlen(g.pool, g.out[:, :3].contiguous(), g.q[:, :3].contiguous(), g.cu_q,
+                             g.cu_k, 4, 8, g.table, w.scale, True)
+    assert e.value.code == -1
     with pytest.raises(ValueError):  # metadata must be int32
         pa.pa_prefill_varlen(g.pool, g.out, g.q, g.cu_q.long(), g.cu_k, 4, 8, g.table, w.scale, True)
+
+
+# --------------------------------------------------------------------------------------
+# fp32 pools: each query token runs as a decode query over its visible keys
+# --------------------------------------------------------------------------------------
+
+F32_SHAPES = [  # (Hq, Hkv, d, B)
+    (4, 2, 64, 32),
+    (8, 4, 128, 16),
+    (8, 8, 64, 16),
+    (8, 1, 128, 32),
+]
+
+
+@pytest.mark.parametrize("shape", F32_SHAPES, ids=lambda s: "-".join(map(str, s)))
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_fp32(shape, causal):
+    hq, hkv, d, B = shape
+    rng = random.Random(hq * 7 + d + B)
+    new = [1, 5, 33, 70, rng.randint(1, 90)]
+    cached = [0, 40, 0, 3, rng.randint(0, 200)]
+    w = W.prefill_workload(cached, new, dtype="f32", num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                           block_size=B, causal=causal, seed=41)
+    _run(w)
+
+
+def test_prefill_fp32_varlen_example_and_masked_blocks(golden):
+    # the varlen example's lengths, q [10, 3, 1] and k [0, 1, 7]: rows with no key are zero
+    gx = golden("varlen_example.json")
+    B, hkv, hq, d = 32, 2, 4, 64
+    gen = torch.Generator().manual_seed(42)
+    kc = torch.randn((4, B, hkv, d), generator=gen)
+    vc = torch.randn((4, B, hkv, d), generator=gen)
+    q = torch.randn((14, hq, d), generator=gen)
+    table = np.array([[-1], [2], [0]], dtype=np.int32)
+    cu_q, cu_k = gx["printed_cu_seq_lens_q"], gx["printed_cu_seq_lens_k"]
+    ref = OA.prefill_varlen(H.storage(q, "f32"), H.storage(kc, "f32"), H.storage(vc, "f32"),
+                            cu_q, cu_k, table, 0.3, True, "f32")
+    pool = pa.KVPool(kc.cuda(), vc.cuda())
+    out = torch.full((14, hq, d), 7.0, device="cuda")
+    pa.pa_prefill_varlen(pool, out, q.cuda(), torch.tensor(cu_q, dtype=torch.int32, device="cuda"),
+                         torch.tensor(cu_k, dtype=torch.int32, device="cuda"),
+                         gx["printed_max_length_q"], gx["printed_max_length_k"],
+                         torch.tensor(table, device="cuda"), 0.3, True)
+    torch.cuda.synchronize()
+    got = H.out_f64(out)
+    H.assert_close(got, ref, "f32", "varlen example, fp32")
+    assert not got[:12].any() and got[12].any() and got[13].any()
+    # an unassigned block and an id beyond the pool inside a request are masked
+    w = W.prefill_workload([40, 100], [20, 30], dtype="f32", num_heads=4, num_kv_heads=2,
+                           head_dim=64, seed=43)
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g, attention=False)
+    o = H.oracle_run(w, attention=False)
+    t = np.asarray(g.plan.tables)
+    t[0, 1] = -1
+    t[1, 3] = 10 ** 6
+    pa.pa_prefill_varlen(g.pool, g.out, g.q, g.cu_q, g.cu_k, g.plan.max_q, g.plan.max_k,
+                         torch.tensor(t, dtype=torch.int32, device="cuda"), w.scale, True)
+    torch.cuda.synchronize()
+    rt = t.copy()
+    rt[1, 3] = -1
+    ref = OA.prefill_varlen(H.storage(w.q, "f32"), o.k_pool, o.v_pool, g.plan.cu_q, g.plan.cu_k,
+                            rt, w.scale, True, "f32")
+    H.assert_close(H.out_f64(g.out), ref, "f32", "fp32 masked blocks")
+
+
+def test_prefill_fp32_matches_bf16_path_on_the_same_values():
+    # the same bf16-representable values through both paths: the fp32 token path and the
+    # MFMA path agree within the bf16 bound (the MFMA path rounds P to bf16)
+    w16 = W.prefill_workload([30, 200, 0], [17, 64, 129], seed=44)
+    g16 = H.gpu_setup(w16)
+    H.gpu_step(w16, g16)
+    w32 = W.prefill_workload([30, 200, 0], [17, 64, 129], seed=44)
+    for name in ("q", "k_ctx", "v_ctx", "k_new", "v_new"):
+        setattr(w32, name, getattr(w16, name).float())
+    w32.dtype = "f32"
+    g32 = H.gpu_setup(w32)
+    H.gpu_step(w32, g32)
+    torch.cuda.synchronize()
+    H.assert_close(H.out_f64(g16.out), H.out_f64(g32.out), "bf16", "fp32 path vs MFMA path")
+    o = H.oracle_run(w32)
+    H.assert_close(H.out_f64(g32.out), o.out, "f32", "fp32 path vs oracle")
 
 
 @pytest.mark.parametrize("seed", [0, 1])
