@@ -493,6 +493,8 @@ int dispatch_shape(int G, const pa_kv_pool* pool, void* out, const void* q, int3
     PA_DECODE_SHAPE(64, 32)
     PA_DECODE_SHAPE(128, 16)
     PA_DECODE_SHAPE(128, 32)
+    PA_DECODE_SHAPE(64, 8)
+    PA_DECODE_SHAPE(128, 8)
 #undef PA_DECODE_SHAPE
     return PA_ERR_UNSUPPORTED;
 }

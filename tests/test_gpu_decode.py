@@ -119,6 +119,10 @@ SHAPES = [  # (dtype, Hq, Hkv, d, B)
     ("f32", 4, 2, 64, 32),
     ("f32", 8, 4, 128, 16),
     ("f32", 4, 4, 128, 32),
+    ("bf16", 16, 8, 128, 8),
+    ("bf16", 8, 1, 64, 8),
+    ("f32", 8, 4, 64, 8),
+    ("f32", 4, 2, 128, 8),
 ]
 
 

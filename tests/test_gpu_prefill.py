@@ -156,7 +156,16 @@ F32_SHAPES = [  # (Hq, Hkv, d, B)
     (8, 4, 128, 16),
     (8, 8, 64, 16),
     (8, 1, 128, 32),
+    (4, 2, 128, 8),
 ]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_bf16_block_size_8(causal):
+    # block size 8 is not a multiple of a wave's 16-key slice: the token path serves it
+    w = W.prefill_workload([0, 13, 50], [9, 40, 3], num_heads=16, num_kv_heads=8, head_dim=128,
+                           block_size=8, causal=causal, seed=45)
+    _run(w)
 
 
 @pytest.mark.parametrize("shape", F32_SHAPES, ids=lambda s: "-".join(map(str, s)))
