@@ -42,10 +42,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 
-// LDS buffers for K/V tiles: 2 stages the next tile while the current one is read.
-#ifndef PA_PREFILL_LDS_BUFFERS
-#define PA_PREFILL_LDS_BUFFERS 2
-#endif
 // Raise the wave's priority while it issues matrix products (1) or not (0).
 #ifndef PA_PREFILL_SETPRIO
 #define PA_PREFILL_SETPRIO 1
@@ -105,9 +101,9 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // rows then cover all banks once, the loader's writes conflict 2-way at most.
     constexpr int PITCH_T = BN + PA_PREFILL_VT_PAD;
     constexpr int LDS_AHEAD = PA_PREFILL_LDS_AHEAD;  // MFMA operands read ahead of use
-    constexpr int NBUF = PA_PREFILL_LDS_BUFFERS;  // 2: the next tile is staged while this one is read
-    __shared__ __align__(16) uint16_t k_lds_all[NBUF][BN * PITCH];
-    __shared__ __align__(16) uint16_t v_lds_all[NBUF][D * PITCH_T];
+    // K/V tiles are double-buffered: the next tile is staged while this one is read
+    __shared__ __align__(16) uint16_t k_lds_all[2][BN * PITCH];
+    __shared__ __align__(16) uint16_t v_lds_all[2][D * PITCH_T];
     uint16_t* const k_lds = k_lds_all[0];
     constexpr int SORT_MAX = BN * PITCH / 2;  // int32 key counts that fit in k_lds
 
@@ -440,50 +436,34 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         if constexpr (PA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
     };
 
-    if constexpr (NBUF == 2) {
-        // one barrier per tile: tile t + 1 is staged into the other buffer after tile t
-        // is computed, while the loads of tile t + 2 are issued
-        uint32_t ok_pend = 0;
-        if (n_tiles > 0) {
-            __syncthreads();  // the request order staged in k_lds is no longer read
-            stage(0);
-            if (n_tiles > 1) {
-                const TileIds next = scalar_ids(1, ids_next);
-                fetch(1, next.wave);
+    // one barrier per tile: tile t + 1 is staged into the other buffer after tile t
+    // is computed, while the loads of tile t + 2 are issued
+    uint32_t ok_pend = 0;
+    if (n_tiles > 0) {
+        __syncthreads();  // the request order staged in k_lds is no longer read
+        stage(0);
+        if (n_tiles > 1) {
+            const TileIds next = scalar_ids(1, ids_next);
+            fetch(1, next.wave);
+            ok_pend = next.bits;
+            if (n_tiles > 2) ids_next = load_ids(2);
+        }
+        __syncthreads();
+    }
+    for (int t = 0; t < n_tiles; ++t) {
+        const int b = t & 1;
+        if (t * BN <= wave_hi) compute(t, b, ok_cur);
+        if (t + 1 < n_tiles) {
+            stage(b ^ 1);
+            ok_cur = ok_pend;
+            if (t + 2 < n_tiles) {
+                const TileIds next = scalar_ids(t + 2, ids_next);
+                fetch(t + 2, next.wave);
                 ok_pend = next.bits;
-                if (n_tiles > 2) ids_next = load_ids(2);
+                if (t + 3 < n_tiles) ids_next = load_ids(t + 3);
             }
-            __syncthreads();
         }
-        for (int t = 0; t < n_tiles; ++t) {
-            const int b = t & 1;
-            if (t * BN <= wave_hi) compute(t, b, ok_cur);
-            if (t + 1 < n_tiles) {
-                stage(b ^ 1);
-                ok_cur = ok_pend;
-                if (t + 2 < n_tiles) {
-                    const TileIds next = scalar_ids(t + 2, ids_next);
-                    fetch(t + 2, next.wave);
-                    ok_pend = next.bits;
-                    if (t + 3 < n_tiles) ids_next = load_ids(t + 3);
-                }
-            }
-            __syncthreads();
-        }
-    } else {
-        for (int t = 0; t < n_tiles; ++t) {
-            __syncthreads();  // the previous tile is no longer read
-            const uint32_t page_ok = ok_cur;
-            stage(0);
-            __syncthreads();
-            if (t + 1 < n_tiles) {  // in flight while this tile is computed
-                const TileIds next = scalar_ids(t + 1, ids_next);
-                fetch(t + 1, next.wave);
-                ok_cur = next.bits;
-                if (t + 2 < n_tiles) ids_next = load_ids(t + 2);
-            }
-            if (t * BN <= wave_hi) compute(t, 0, page_ok);  // else no row of this wave sees the tile
-        }
+        __syncthreads();
     }
 
     // normalise and store: lane holds d = 32db + 8i + 4h + jj of its row
