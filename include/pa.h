@@ -141,6 +141,29 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
               void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * The two passes of pa_decode as separate calls (split-K decoding: partial states per
+ * partition, then their merge by the [PA11] §11.2 rule), for callers that schedule
+ * them apart or time them apart.  pa_decode_partials takes pa_decode's arguments plus
+ * optional k_new, v_new (both NULL, or both given as for pa_decode_append); it finishes
+ * the sequences that fit in one partition and leaves the others' partial states in the
+ * workspace.  pa_decode_merge must follow on the same stream with the same pool, out,
+ * batch, num_heads, max_blocks_per_seq, seqlens_k, max_seqlen_k, partition_tokens and
+ * workspace (it reads the partials and writes the remaining rows; nothing to do when
+ * no sequence was split).  pa_decode_partials then pa_decode_merge = pa_decode, bit
+ * for bit.
+ * ------------------------------------------------------------------------------- */
+int pa_decode_partials(const pa_kv_pool* pool, void* out, const void* q, const void* k_new,
+                       const void* v_new, int32_t batch, int32_t num_heads,
+                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* seqlens_k, int32_t max_seqlen_k, float softmax_scale,
+                       int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream);
+int pa_decode_merge(const pa_kv_pool* pool, void* out, int32_t batch, int32_t num_heads,
+                    int32_t max_blocks_per_seq, const int32_t* seqlens_k, int32_t max_seqlen_k,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Decode with the KV write fused in ([HFPA] Çözme yolu: the decode kernel reads the cache
  * through block_table and updates it in place).  Same arguments and result as
  * pa_decode, plus k_new, v_new: device [batch][Hkv][d], the current token's K and V.

@@ -29,7 +29,7 @@ EXPORTS = [
     "pa_bm_prepare_write", "pa_build_slot_mapping", "pa_build_cu_seqlens", "pa_pool_bytes",
     "pa_validate_decode", "pa_validate_varlen", "pa_validate_slots", "pa_probe_stream_read",
     "pa_prefix_block_hash", "pa_bm_allocate_prefix", "pa_decode_append",
-    "pa_prefill_varlen_contiguous",
+    "pa_prefill_varlen_contiguous", "pa_decode_partials", "pa_decode_merge",
 ]
 
 
@@ -88,6 +88,11 @@ def lib() -> ctypes.CDLL:
         "pa_decode_append": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _VP, _VP, _I32, _I32, _VP,
                                             _I32, _VP, _I32, ctypes.c_float, _I32, _VP,
                                             ctypes.c_size_t, _VP]),
+        "pa_decode_partials": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _VP, _VP, _I32, _I32,
+                                              _VP, _I32, _VP, _I32, ctypes.c_float, _I32, _VP,
+                                              ctypes.c_size_t, _VP]),
+        "pa_decode_merge": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _I32, _I32, _I32, _VP, _I32,
+                                           _I32, _VP, ctypes.c_size_t, _VP]),
         "pa_prefill_varlen": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP, _VP,
                                              _I32, _I32, _VP, _I32, ctypes.c_float, _I32, _VP]),
         "pa_prefill_varlen_contiguous": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
@@ -251,6 +256,35 @@ def pa_decode_append(pool: KVPool, out, q, k_new, v_new, block_table, seqlens_k,
                                 _dev(workspace, "workspace"), ws_bytes, _stream(stream))
     if st:
         _raise(st, "pa_decode_append")
+
+
+def pa_decode_partials(pool: KVPool, out, q, block_table, seqlens_k, max_seqlen_k: int,
+                       softmax_scale: float, partition_tokens: int = 0, workspace=None,
+                       k_new=None, v_new=None, stream=None) -> None:
+    """Pass 1 of pa_decode (optionally with the fused append); pa_decode_merge follows."""
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pa_decode_partials(ctypes.byref(pool.struct), _dev(out, "out"), _dev(q, "q"),
+                                  _dev(k_new, "k_new"), _dev(v_new, "v_new"), batch, hq,
+                                  _meta(block_table, "block_table"), int(block_table.shape[1]),
+                                  _meta(seqlens_k, "seqlens_k"), int(max_seqlen_k),
+                                  float(softmax_scale), int(partition_tokens),
+                                  _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    if st:
+        _raise(st, "pa_decode_partials")
+
+
+def pa_decode_merge(pool: KVPool, out, block_table, seqlens_k, max_seqlen_k: int,
+                    partition_tokens: int = 0, workspace=None, stream=None) -> None:
+    """Pass 2 of pa_decode, with the arguments of the pa_decode_partials call before it."""
+    batch, hq = int(out.shape[0]), int(out.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pa_decode_merge(ctypes.byref(pool.struct), _dev(out, "out"), batch, hq,
+                               int(block_table.shape[1]), _meta(seqlens_k, "seqlens_k"),
+                               int(max_seqlen_k), int(partition_tokens),
+                               _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    if st:
+        _raise(st, "pa_decode_merge")
 
 
 def pa_prefill_varlen(pool: KVPool, out, q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,

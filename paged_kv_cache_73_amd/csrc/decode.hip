@@ -83,6 +83,10 @@ __device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[E], int
     m = m_new;
 }
 
+// The two passes of a split-K decode: partial states (and the rows of single-partition
+// sequences), then their merge.
+constexpr int kPass1 = 1, kPass2 = 2;
+
 // Packed query tokens in place of sequences (the varlen prefill run token by token):
 // "sequence" b is query token offset + blockIdx.z of the packed batch, its request is
 // the one whose [cu_q[i], cu_q[i+1]) holds it, and it attends to that request's first
@@ -416,8 +420,11 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
 // sequence; the aim is about kTargetWorkgroups workgroups in total (seven per CU of the
 // 256 on an MI355X: enough to keep every CU fed, few enough that each streams a long
 // run of pages and the merge stays small), assuming contexts average 60 % of the
-// maximum.  Rounded to 64 tokens and kept within [128, 4096].
+// maximum, and no shorter than max_seqlen_k / kMaxAutoParts (to 64 tokens) so that the
+// longest sequences are not cut into very many partitions.  Rounded to 64 tokens and
+// kept within [128, 4096].
 constexpr int64_t kTargetWorkgroups = 7 * 256;
+constexpr int64_t kMaxAutoParts = 64;
 
 inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size, int32_t batch,
                               int32_t num_kv_heads, int32_t max_seqlen_k) {
@@ -427,6 +434,8 @@ inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size, int3
     const int64_t groups = num_kv_heads / per_wg;
     const int64_t est_keys = static_cast<int64_t>(batch) * max_seqlen_k * 6 / 10;
     int64_t p = (est_keys * groups / kTargetWorkgroups + 63) / 64 * 64;
+    // about kMaxAutoParts partitions per sequence at most: the merge reads each one's state
+    p = std::max<int64_t>(p, (static_cast<int64_t>(max_seqlen_k) / kMaxAutoParts + 32) / 64 * 64);
     p = std::max<int64_t>(128, std::min<int64_t>(4096, p));
     return static_cast<int32_t>((p + block_size - 1) / block_size * block_size);
 }
@@ -436,19 +445,19 @@ int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batc
                   int32_t num_heads, const int32_t* table, int32_t max_blocks,
                   const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
                   int32_t part_tokens, float scale, float* o_part, float* ml_part, hipStream_t stream,
-                  const TokenMap& tm) {
+                  const TokenMap& tm, int passes) {
     const int hkv = pool->num_kv_heads;
     int per_wg = PA_DECODE_HPW;
     while (hkv % per_wg != 0) per_wg >>= 1;
     const dim3 grid(hkv / per_wg, max_parts, batch);
-    hipLaunchKernelGGL((decode_partial_kernel<T, D, BS, G>), grid, dim3(per_wg * kWave), 0, stream,
+    if (passes & kPass1) hipLaunchKernelGGL((decode_partial_kernel<T, D, BS, G>), grid, dim3(per_wg * kWave), 0, stream,
                        static_cast<const T*>(q), static_cast<char*>(pool->k_cache),
                        static_cast<char*>(pool->v_cache), table, seqlens,
                        static_cast<const T*>(k_new), static_cast<const T*>(v_new),
                        static_cast<T*>(out), o_part, ml_part, num_heads, hkv, pool->num_blocks,
                        max_blocks, max_parts, part_tokens / BS, scale * kLog2e, tm);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-    if (max_parts > 1) {
+    if ((passes & kPass2) && max_parts > 1) {
         hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(num_heads, batch), dim3(kWave), 0,
                            stream, seqlens, o_part, ml_part, static_cast<T*>(out), num_heads,
                            max_blocks * BS, max_parts, part_tokens);
@@ -461,12 +470,12 @@ int dispatch_group(int G, const pa_kv_pool* pool, void* out, const void* q, int3
                    int32_t num_heads, const int32_t* table, int32_t max_blocks,
                    const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
                    int32_t part_tokens, float scale, float* o_part, float* ml_part,
-                   hipStream_t stream, const TokenMap& tm) {
+                   hipStream_t stream, const TokenMap& tm, int passes) {
 #define PA_DECODE_G(GG)                                                                    \
     case GG:                                                                               \
         return launch_decode<T, D, BS, GG>(pool, out, q, batch, num_heads, table, max_blocks, \
                                            seqlens, k_new, v_new, max_parts, part_tokens,    \
-                                           scale, o_part, ml_part, stream, tm);
+                                           scale, o_part, ml_part, stream, tm, passes);
     switch (G) {
         PA_DECODE_G(1)
         PA_DECODE_G(2)
@@ -482,13 +491,13 @@ int dispatch_shape(int G, const pa_kv_pool* pool, void* out, const void* q, int3
                    int32_t num_heads, const int32_t* table, int32_t max_blocks,
                    const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
                    int32_t part_tokens, float scale, float* o_part, float* ml_part,
-                   hipStream_t stream, const TokenMap& tm) {
+                   hipStream_t stream, const TokenMap& tm, int passes) {
     const int D = pool->head_dim, BS = pool->block_size;
 #define PA_DECODE_SHAPE(DD, BB)                                                             \
     if (D == DD && BS == BB)                                                                \
         return dispatch_group<T, DD, BB>(G, pool, out, q, batch, num_heads, table, max_blocks, \
                                          seqlens, k_new, v_new, max_parts, part_tokens,       \
-                                         scale, o_part, ml_part, stream, tm);
+                                         scale, o_part, ml_part, stream, tm, passes);
     PA_DECODE_SHAPE(64, 16)
     PA_DECODE_SHAPE(64, 32)
     PA_DECODE_SHAPE(128, 16)
@@ -528,15 +537,15 @@ int decode_impl(const pa_kv_pool* pool, void* out, const void* q, const void* k_
                 const void* v_new, int32_t batch, int32_t num_heads, const int32_t* block_table,
                 int32_t max_blocks_per_seq, const int32_t* seqlens_k, int32_t max_seqlen_k,
                 float softmax_scale, int32_t partition_tokens, void* workspace,
-                size_t workspace_size, void* stream) {
+                size_t workspace_size, void* stream, int passes) {
     int st = check_pool(pool);
     if (st != PA_OK) return st;
     if (batch < 0 || num_heads <= 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0 ||
         partition_tokens < 0)
         return PA_ERR_INVALID_ARG;
     if (batch == 0) return PA_OK;
-    if (out == nullptr || q == nullptr || seqlens_k == nullptr ||
-        (max_blocks_per_seq > 0 && block_table == nullptr))
+    if (out == nullptr || seqlens_k == nullptr ||
+        ((passes & kPass1) && (q == nullptr || (max_blocks_per_seq > 0 && block_table == nullptr))))
         return PA_ERR_INVALID_ARG;
     if (num_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
     if (pool->num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
@@ -560,10 +569,11 @@ int decode_impl(const pa_kv_pool* pool, void* out, const void* q, const void* k_
     if (pool->dtype == PA_BF16)
         return dispatch_shape<bf16_t>(G, pool, out, q, batch, num_heads, block_table,
                                       max_blocks_per_seq, seqlens_k, k_new, v_new, max_parts,
-                                      part_tokens, softmax_scale, o_part, ml_part, s, TokenMap{});
+                                      part_tokens, softmax_scale, o_part, ml_part, s, TokenMap{},
+                                      passes);
     return dispatch_shape<float>(G, pool, out, q, batch, num_heads, block_table,
                                  max_blocks_per_seq, seqlens_k, k_new, v_new, max_parts,
-                                 part_tokens, softmax_scale, o_part, ml_part, s, TokenMap{});
+                                 part_tokens, softmax_scale, o_part, ml_part, s, TokenMap{}, passes);
 }
 
 // The varlen prefill run one packed query token at a time by the decode kernel, each
@@ -590,10 +600,10 @@ int prefill_by_token(const pa_kv_pool* pool, void* out, const void* q, int32_t b
         const int st = pool->dtype == PA_BF16
             ? dispatch_shape<bf16_t>(G, pool, out, q, n, num_heads, block_table, max_blocks,
                                      nullptr, nullptr, nullptr, 1, part_tokens, scale, nullptr,
-                                     nullptr, s, tm)
+                                     nullptr, s, tm, kPass1 | kPass2)
             : dispatch_shape<float>(G, pool, out, q, n, num_heads, block_table, max_blocks,
                                     nullptr, nullptr, nullptr, 1, part_tokens, scale, nullptr,
-                                    nullptr, s, tm);
+                                    nullptr, s, tm, kPass1 | kPass2);
         if (st != PA_OK) return st;
     }
     return PA_OK;
@@ -608,7 +618,30 @@ extern "C" int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32
                          void* workspace, size_t workspace_size, void* stream) {
     return pa::decode_impl(pool, out, q, nullptr, nullptr, batch, num_heads, block_table,
                            max_blocks_per_seq, seqlens_k, max_seqlen_k, softmax_scale,
-                           partition_tokens, workspace, workspace_size, stream);
+                           partition_tokens, workspace, workspace_size, stream,
+                           pa::kPass1 | pa::kPass2);
+}
+
+extern "C" int pa_decode_partials(const pa_kv_pool* pool, void* out, const void* q,
+                                  const void* k_new, const void* v_new, int32_t batch,
+                                  int32_t num_heads, const int32_t* block_table,
+                                  int32_t max_blocks_per_seq, const int32_t* seqlens_k,
+                                  int32_t max_seqlen_k, float softmax_scale,
+                                  int32_t partition_tokens, void* workspace,
+                                  size_t workspace_size, void* stream) {
+    if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_INVALID_ARG;
+    return pa::decode_impl(pool, out, q, k_new, v_new, batch, num_heads, block_table,
+                           max_blocks_per_seq, seqlens_k, max_seqlen_k, softmax_scale,
+                           partition_tokens, workspace, workspace_size, stream, pa::kPass1);
+}
+
+extern "C" int pa_decode_merge(const pa_kv_pool* pool, void* out, int32_t batch, int32_t num_heads,
+                               int32_t max_blocks_per_seq, const int32_t* seqlens_k,
+                               int32_t max_seqlen_k, int32_t partition_tokens, void* workspace,
+                               size_t workspace_size, void* stream) {
+    return pa::decode_impl(pool, out, nullptr, nullptr, nullptr, batch, num_heads, nullptr,
+                           max_blocks_per_seq, seqlens_k, max_seqlen_k, 1.f, partition_tokens,
+                           workspace, workspace_size, stream, pa::kPass2);
 }
 
 extern "C" int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q,
@@ -621,5 +654,6 @@ extern "C" int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q
     if (batch > 0 && (k_new == nullptr || v_new == nullptr)) return PA_ERR_INVALID_ARG;
     return pa::decode_impl(pool, out, q, k_new, v_new, batch, num_heads, block_table,
                            max_blocks_per_seq, seqlens_k, max_seqlen_k, softmax_scale,
-                           partition_tokens, workspace, workspace_size, stream);
+                           partition_tokens, workspace, workspace_size, stream,
+                           pa::kPass1 | pa::kPass2);
 }

@@ -94,6 +94,20 @@ def attend_contiguous(w: W.Workload, r: DeviceRun, k: torch.Tensor, v: torch.Ten
                                     w.scale, w.causal)
 
 
+def attend_partials(w: W.Workload, r: DeviceRun, partition_tokens: int = 0) -> None:
+    """Pass 1 of the decode (pa_decode_partials); attend_merge completes it."""
+    ensure_workspace(w, r, partition_tokens)
+    max_k = max(r.plan.seqlens_k) if r.plan.seqlens_k else 0
+    pa.pa_decode_partials(r.pool, r.out, r.q, r.table, r.seqlens, max_k, w.scale,
+                          partition_tokens, r.workspace)
+
+
+def attend_merge(w: W.Workload, r: DeviceRun, partition_tokens: int = 0) -> None:
+    """Pass 2 of the decode (pa_decode_merge)."""
+    max_k = max(r.plan.seqlens_k) if r.plan.seqlens_k else 0
+    pa.pa_decode_merge(r.pool, r.out, r.table, r.seqlens, max_k, partition_tokens, r.workspace)
+
+
 def attend_append(w: W.Workload, r: DeviceRun, partition_tokens: int = 0) -> None:
     """Decode with the new tokens' K/V stored by the attention launch itself."""
     if w.kind != "decode":

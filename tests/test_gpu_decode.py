@@ -302,6 +302,38 @@ def test_decode_append_edge_cases():
     assert e.value.code == -1
 
 
+@pytest.mark.parametrize("partition_tokens", [0, 64, 256])
+def test_decode_two_passes_equal_one_call(partition_tokens):
+    w = W.decode_workload([0, 1, 100, 700, 2047, 3000, 16], dtype="bf16", seed=23)
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g, partition_tokens)
+    torch.cuda.synchronize()
+    whole = g.out.clone()
+    g.out.fill_(7.0)
+    max_k = max(g.plan.seqlens_k)
+    pa.pa_decode_partials(g.pool, g.out, g.q, g.table, g.seqlens, max_k, w.scale, partition_tokens,
+                          g.workspace)
+    pa.pa_decode_merge(g.pool, g.out, g.table, g.seqlens, max_k, partition_tokens, g.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(g.out, whole)
+    # with the append: the same as pa_decode_append
+    sep = H.gpu_setup(w)
+    H.gpu_step(w, sep, partition_tokens, fused=True)
+    two = H.gpu_setup(w)
+    two.workspace = torch.zeros_like(g.workspace)
+    pa.pa_decode_partials(two.pool, two.out, two.q, two.table, two.seqlens, max_k, w.scale,
+                          partition_tokens, two.workspace, k_new=two.k_new, v_new=two.v_new)
+    pa.pa_decode_merge(two.pool, two.out, two.table, two.seqlens, max_k, partition_tokens,
+                       two.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(two.out, sep.out)
+    assert torch.equal(two.k_cache.view(torch.int16), sep.k_cache.view(torch.int16))
+    with pytest.raises(pa.PaError) as e:   # k_new without v_new
+        pa.pa_decode_partials(two.pool, two.out, two.q, two.table, two.seqlens, max_k, w.scale,
+                              partition_tokens, two.workspace, k_new=two.k_new)
+    assert e.value.code == -1
+
+
 # --------------------------------------------------------------------------------------
 # the full-size workloads
 # --------------------------------------------------------------------------------------
