@@ -60,6 +60,8 @@ constexpr int kPrefillKeys = 64;    // keys per tile
 constexpr int kPrefillThreads = 256;
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X
 constexpr float kRescaleSlack = 8.f; // weights stay below 2^8 between rescales
+constexpr int kMaxRankedRequests = 256;  // requests ordered by key count in-kernel
+constexpr int kMaxRankedJobs = 1024;     // jobs per XCD ordered by key tiles in-kernel
 
 // Instruction order for a run of N products whose operands come from LDS: AHEAD reads
 // first, then each product followed by the next read, so that AHEAD reads stay in
@@ -104,48 +106,90 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // K/V tiles are double-buffered: the next tile is staged while this one is read
     __shared__ __align__(16) uint16_t k_lds_all[2][BN * PITCH];
     __shared__ __align__(16) uint16_t v_lds_all[2][D * PITCH_T];
-    uint16_t* const k_lds = k_lds_all[0];
-    constexpr int SORT_MAX = BN * PITCH / 2;  // int32 key counts that fit in k_lds
+    static_assert(2 * kMaxRankedRequests <= BN * PITCH / 2 && kMaxRankedJobs <= BN * PITCH / 2,
+                  "the ranking tables fit in one K tile buffer each");
 
-    // Workgroups are handed to the 8 XCDs round-robin (id L runs on XCD L % 8).  All
-    // query tiles of one (request, KV head) group read the same K/V pages, so they are
-    // kept on one XCD (sharing its L2): group g runs on XCD g % 8, and each XCD walks its
-    // groups in order, the query tiles of a group back to back.
+    // Work items are jobs (group, query tile), a group being one (request, KV head).
+    // Workgroup L runs on XCD L % 8 (workgroups are handed to the XCDs round-robin), and
+    // the jobs of group g all run on XCD g % 8: the query tiles of a group read the same
+    // K/V pages, which then stay in that XCD's L2.  Requests are ranked by key count,
+    // longest first, and group g belongs to the request of rank g / Hkv, so that every
+    // request's heads are spread over the 8 XCDs.  Within an XCD the jobs start in order
+    // of decreasing key-tile count (longest-processing-time first): workgroup slot s of
+    // the XCD takes the job of rank s, and the short jobs fill the gaps at the end.
+    // Every workgroup derives the same orders from cu_q / cu_k in LDS (the K tile
+    // buffers, overwritten only after a barrier); beyond kMaxRankedRequests requests or
+    // kMaxRankedJobs jobs per XCD the batch order is kept instead.
     const int L = blockIdx.x;
+    const int xcd = L % kXcds;
     const int slot = L / kXcds;
-    const int group = (slot / n_qtiles) * kXcds + L % kXcds;
-    if (group >= n_groups) return;  // grid padding
-    const int hkv = group % num_kv_heads;
     const int tid = threadIdx.x;
-    // Groups are taken in order of decreasing key count (longest-first scheduling): the
-    // request of rank r in that order is the one with r requests ahead of it (longer,
-    // or as long and earlier in the batch).  Every workgroup derives the same order
-    // from cu_k; the key counts are staged in the K tile's LDS, which the loop below
-    // overwrites only after a barrier.
     const int batch = n_groups / num_kv_heads;
-    const int rank = group / num_kv_heads;
-    int req = rank;
-    if (batch > 1 && batch <= SORT_MAX) {  // larger batches keep their own order
-        __shared__ int32_t found;
-        int32_t* klen = reinterpret_cast<int32_t*>(k_lds);
+    const int n_jobs = (n_groups + kXcds - 1) / kXcds * n_qtiles;  // workgroups per XCD
+    // key tiles of a job: -1 when its first token is past the request's queries
+    auto job_tiles = [&](int req, int tok0) {
+        const int q_len = cu_q[req + 1] - cu_q[req];
+        if (tok0 >= q_len) return -1;
+        const int k_len_req = cu_k[req + 1] - cu_k[req];
+        const int k_len = kPaged ? min(k_len_req, max_blocks * BS) : k_len_req;
+        const int tok_last = min(tok0 + TOK, q_len) - 1;
+        const int kv_end = causal ? min(k_len, k_len_req - q_len + tok_last + 1) : k_len;
+        return (kv_end > 0 && (!kPaged || num_blocks > 0)) ? (kv_end + BN - 1) / BN : 0;
+    };
+    const bool rank_requests = batch > 1 && batch <= kMaxRankedRequests;
+    const bool rank_jobs = n_jobs > 1 && n_jobs <= kMaxRankedJobs;
+    int32_t* const perm = reinterpret_cast<int32_t*>(k_lds_all[0]);  // request of each rank
+    int32_t* const klen = perm + kMaxRankedRequests;                 // key count of each request
+    int32_t* const jobs = reinterpret_cast<int32_t*>(k_lds_all[1]);  // key tiles of each job
+    __shared__ int32_t found;
+    if (rank_requests) {
         for (int j = tid; j < batch; j += kPrefillThreads) klen[j] = cu_k[j + 1] - cu_k[j];
         __syncthreads();
         for (int j = tid; j < batch; j += kPrefillThreads) {
             const int kj = klen[j];
-            int ahead = 0;
+            int ahead = 0;  // requests before j in the order: longer, or as long and earlier
             for (int i = 0; i < batch; ++i) {
                 const int ki = klen[i];
                 ahead += (ki > kj) | ((ki == kj) & (i < j));
             }
-            if (ahead == rank) found = j;
+            perm[ahead] = j;
         }
         __syncthreads();
-        req = __builtin_amdgcn_readfirstlane(found);  // uniform: keeps the addressing scalar
     }
+    auto request_of = [&](int rank) { return rank_requests ? perm[rank] : rank; };
+    int group, qtile;
+    if (rank_jobs) {
+        // job c of this XCD: group (c / n_qtiles) * 8 + xcd, query tile c % n_qtiles
+        for (int c = tid; c < n_jobs; c += kPrefillThreads) {
+            const int g = (c / n_qtiles) * kXcds + xcd;
+            jobs[c] = g < n_groups ? job_tiles(request_of(g / num_kv_heads), (c % n_qtiles) * TOK) : -1;
+        }
+        __syncthreads();
+        for (int c = tid; c < n_jobs; c += kPrefillThreads) {
+            const int v = jobs[c];
+            int ahead = 0;  // jobs before c: more tiles, or as many and a lower index
+            for (int i = 0; i < n_jobs; ++i) {
+                const int u = jobs[i];
+                ahead += (u > v) | ((u == v) & (i < c));
+            }
+            if (ahead == slot) found = c;
+        }
+        __syncthreads();
+        const int c = __builtin_amdgcn_readfirstlane(found);
+        group = (c / n_qtiles) * kXcds + xcd;
+        qtile = c % n_qtiles;
+    } else {
+        // the groups of the XCD in turn, the query tiles of a group back to back, the
+        // later ones (which see more keys under the causal mask) first
+        group = (slot / n_qtiles) * kXcds + xcd;
+        qtile = n_qtiles - 1 - slot % n_qtiles;
+    }
+    if (group >= n_groups) return;  // uniform: grid padding
+    const int hkv = group % num_kv_heads;
+    const int req = __builtin_amdgcn_readfirstlane(request_of(group / num_kv_heads));  // scalar addressing
     const int q0 = cu_q[req];
     const int q_len = cu_q[req + 1] - q0;
-    // later query tiles see more keys under the causal mask: start them first
-    const int tok0 = (n_qtiles - 1 - slot % n_qtiles) * TOK;
+    const int tok0 = qtile * TOK;
     if (tok0 >= q_len) return;  // uniform: tile past this request's queries
     const int k_len_req = cu_k[req + 1] - cu_k[req];
     const int cached = k_len_req - q_len;                       // may be negative
@@ -153,7 +197,6 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int tok_last = min(tok0 + TOK, q_len) - 1;
     const int kv_end = causal ? min(k_len, cached + tok_last + 1) : k_len;
     const int n_tiles = (kv_end > 0 && (!kPaged || num_blocks > 0)) ? (kv_end + BN - 1) / BN : 0;
-
     const int lane = tid % kWave;
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave index, kept in a scalar
     const int h = lane / 32;      // which 8-wide half of a 16-wide k-step this lane feeds
@@ -440,7 +483,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // is computed, while the loads of tile t + 2 are issued
     uint32_t ok_pend = 0;
     if (n_tiles > 0) {
-        __syncthreads();  // the request order staged in k_lds is no longer read
+        __syncthreads();  // the orders staged in the K tile buffers are no longer read
         stage(0);
         if (n_tiles > 1) {
             const TileIds next = scalar_ids(1, ids_next);
