@@ -135,7 +135,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="qwen3_decode_b64", choices=WORKLOADS)
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)

@@ -328,13 +328,19 @@ def test_contiguous_prefill_full_size():
     _contiguous_case(w, requests=[0, 5, 11, 15])
 
 
-@pytest.mark.parametrize("batch", [300, 2400])
-def test_prefill_many_requests(batch):
-    # many short requests: the longest-first order covers batches up to its limit (2304
-    # requests at d = 64) and larger ones keep the batch order; both give the same rows
-    rng = random.Random(batch)
-    new = [rng.randint(1, 3) for _ in range(batch)]
+@pytest.mark.parametrize("batch,q_hi,num_heads,num_kv_heads", [
+    (300, 3, 4, 2),     # requests in batch order, jobs ranked (75 jobs per XCD)
+    (2400, 3, 4, 2),    # requests in batch order, jobs ranked (600 per XCD)
+    (2400, 100, 4, 2),  # both in batch order (1200 jobs per XCD)
+    (256, 320, 16, 8),  # requests ranked, jobs in group order (1280 jobs per XCD)
+])
+def test_prefill_many_requests(batch, q_hi, num_heads, num_kv_heads):
+    # The kernel ranks requests by key count up to 256 requests and the jobs of an XCD by
+    # key tiles up to 1024 jobs; past either limit it keeps the batch / group order.  Every
+    # order must give the same rows.
+    rng = random.Random(batch * 1000 + q_hi)
+    new = [rng.randint(1, q_hi) for _ in range(batch)]
     cached = [rng.randint(0, 40) for _ in range(batch)]
-    w = W.prefill_workload(cached, new, num_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
-                           seed=33)
+    w = W.prefill_workload(cached, new, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                           head_dim=64, block_size=16, seed=33)
     _run(w, requests=list(range(0, batch, 7)))
