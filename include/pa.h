@@ -38,7 +38,7 @@
  *   returns PA_ERR_HIP.  The contents of device metadata (tables, lengths, slots)
  *   are not validated by the device calls (that would need a synchronisation);
  *   the pa_validate_* functions check host copies of them.
- * - Supported: dtype F32 or BF16, head_dim 64 or 128, block_size 8, 16 or 32,
+ * - Supported: dtype F32 or BF16, head_dim 64 or 128, block_size 2, 4, 8, 16 or 32,
  *   num_heads / num_kv_heads in {1, 2, 4, 8}, num_kv_heads <= 64.  Other shapes
  *   return PA_ERR_UNSUPPORTED.
  */
@@ -119,6 +119,8 @@ int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src, const int32_t* ds
  * max_seqlen_k: host bound on seqlens_k, sizes the grid and the workspace.
  * partition_tokens: split-K partition length (a multiple of B), or 0 for an automatic
  *   choice from batch, num_kv_heads and max_seqlen_k (about seven workgroups per CU).
+ *   It is rounded up to a multiple of max(B, 1024 / (2 * head_dim)), the keys one
+ *   16-byte load per lane covers, which matters only for block_size 2 and 4.
  *   Keys are cut into partitions processed by different workgroups; each yields an
  *   online-softmax state (m, l, o) and a second kernel merges them with the [PA11]
  *   §11.2 rule.  Sequences with one partition are finished by the first kernel.
@@ -188,8 +190,8 @@ int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q, const voi
  *
  * q, out: device, [total_q][num_heads][d] with total_q = cu_seqlens_q[batch], in the
  *   pool's dtype.  BF16 pools with block_size 16 or 32 run on the matrix cores; F32 pools
- *   and block_size 8 run each query token as a decode query over its visible keys (no
- *   matrix cores, one partition per token).
+ *   and block_size 2, 4 or 8 run each query token as a decode query over its visible keys
+ *   (no matrix cores, one partition per token).
  * cu_seqlens_q, cu_seqlens_k: device int32 [batch+1], non-decreasing from 0.  Request
  *   i owns query rows [cu_q[i], cu_q[i+1]) and k_len = cu_k[i+1]-cu_k[i] keys, read
  *   through block_table row i (only the differences of cu_k are used; the new tokens'
@@ -199,7 +201,7 @@ int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q, const voi
  * max_seqlen_q, max_seqlen_k: host bounds on the per-request lengths (grid sizing);
  *   queries of a request beyond max_seqlen_q are not computed.
  * softmax_scale must be positive and finite (PA_ERR_INVALID_ARG otherwise).
- * Supported: BF16 or F32 pools, head_dim 64 or 128, block_size 8, 16 or 32, num_heads /
+ * Supported: BF16 or F32 pools, head_dim 64 or 128, block_size 2, 4, 8, 16 or 32, num_heads /
  *   num_kv_heads in {1, 2, 4, 8}, and on the token path num_kv_heads <= 64; otherwise
  *   PA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------------- */

@@ -59,10 +59,16 @@ struct PageShape {
     static constexpr int kRowBytes = D * kElemBytes;
     static constexpr int kLanesPerRow = kRowBytes / 16;      // LPR
     static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
-    static constexpr int kLoads = BS / kRowsPerLoad;         // load instructions per page
+    // Pages of fewer rows than one load covers (block size 2 or 4) are walked as "virtual
+    // pages" of kRowsPerLoad keys, each lane loading its row from its own block.
+    static constexpr bool kSmall = BS < kRowsPerLoad;
+    static constexpr int kPagesPerStep = kSmall ? kRowsPerLoad / BS : 1;  // VP
+    static constexpr int kStepKeys = BS * kPagesPerStep;     // keys per (virtual) page
+    static constexpr int kLoads = kStepKeys / kRowsPerLoad;  // load instructions per page
     static constexpr int kElems = 16 / kElemBytes;           // values per lane per load
     static_assert(kLanesPerRow >= 1 && kLanesPerRow <= kWave, "row size");
-    static_assert(BS % kRowsPerLoad == 0, "block size vs rows per load");
+    static_assert(kSmall ? kRowsPerLoad % BS == 0 : BS % kRowsPerLoad == 0,
+                  "block size vs rows per load");
 };
 
 // Merge (m, l, o) with the state held by the lane `off` positions away (xor).
@@ -119,6 +125,8 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     constexpr int LPR = S::kLanesPerRow;
     constexpr int RPL = S::kRowsPerLoad;
     constexpr int NL = S::kLoads;
+    constexpr int VP = S::kPagesPerStep;  // pages per step (1 unless pages are small)
+    constexpr int SK = S::kStepKeys;      // keys per step
     constexpr int E = S::kElems;
 
     const int lane = threadIdx.x % kWave;
@@ -205,10 +213,11 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     // Consume one page of K/V already in registers.  A page whose block id is outside
     // [0, num_blocks) was loaded from block 0 instead and is masked entirely.  Values are
     // widened to fp32 one 16-byte piece at a time to keep few registers live.
+    // With small pages the id is this lane's own block and every row is checked.
     auto consume = [&](int32_t id, int32_t tok0, const uint4 (&kb)[NL], const uint4 (&vb)[NL]) {
         const bool valid = id >= 0 && id < num_blocks;
-        const bool partial = !valid || tok0 + BS > t_end;
-        const bool has_new = appending && tok0 + BS > new_pos;  // uniform: the last page
+        const bool partial = S::kSmall || !valid || tok0 + SK > t_end;
+        const bool has_new = appending && tok0 + SK > new_pos;  // uniform: the last page
         auto piece = [&](const uint4 (&buf)[NL], const uint4& fresh, int j) {
             uint4 x = buf[j];
             if (has_new && tok0 + r0 + j * RPL == new_pos) x = fresh;
@@ -275,6 +284,13 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     // page: one 32-bit lane offset, the row step in the scalar offset, and accesses the
     // hardware bounds-checks against the page.  Invalid ids read block 0 instead.
     auto load_page = [&](int32_t id, uint4 (&kd)[NL], uint4 (&vd)[NL]) {
+        if constexpr (S::kSmall) {  // one row per lane group, each from its own block
+            const int64_t at = static_cast<int64_t>((id >= 0 && id < num_blocks) ? id : 0) * page_bytes +
+                               ((r0 % BS) * num_kv_heads + hkv) * S::kRowBytes + c * 16;
+            kd[0] = *reinterpret_cast<const uint4*>(k_cache + at);
+            vd[0] = *reinterpret_cast<const uint4*>(v_cache + at);
+            return;
+        }
         const int64_t base = static_cast<int64_t>((id >= 0 && id < num_blocks) ? id : 0) * page_bytes;
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>(k_cache + base), 0, static_cast<int32_t>(page_bytes), kBufferDword3);
@@ -288,28 +304,33 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
 
     if (num_blocks <= 0) pg1 = pg0;  // nothing can be read
     for (int32_t pc = pg0; pc < pg1; pc += kWave) {
-        const int np = min(kWave, pg1 - pc);
-        const int32_t my_id = (lane < np) ? table_row[pc + lane] : -1;
+        const int np = (min(kWave, pg1 - pc) + VP - 1) / VP;  // (virtual) pages of the chunk
+        const int32_t my_id = (lane < min(kWave, pg1 - pc)) ? table_row[pc + lane] : -1;
+        // id of step i: a scalar, or with small pages this lane's block
+        auto step_id = [&](int i) -> int32_t {
+            if constexpr (S::kSmall) return __shfl(my_id, i * VP + r0 / BS);
+            else return __builtin_amdgcn_readlane(my_id, i);
+        };
         // ping-pong: while one page is consumed the next one is in flight
         uint4 ka[NL], va[NL], kb[NL], vb[NL];
-        int32_t id_a = __builtin_amdgcn_readlane(my_id, 0);
+        int32_t id_a = step_id(0);
         load_page(id_a, ka, va);
         int i = 0;
         for (; i + 2 < np; i += 2) {
-            const int32_t id_b = __builtin_amdgcn_readlane(my_id, i + 1);
+            const int32_t id_b = step_id(i + 1);
             load_page(id_b, kb, vb);
-            consume(id_a, (pc + i) * BS, ka, va);
-            id_a = __builtin_amdgcn_readlane(my_id, i + 2);
+            consume(id_a, (pc + i * VP) * BS, ka, va);
+            id_a = step_id(i + 2);
             load_page(id_a, ka, va);
-            consume(id_b, (pc + i + 1) * BS, kb, vb);
+            consume(id_b, (pc + (i + 1) * VP) * BS, kb, vb);
         }
         if (i + 1 < np) {
-            const int32_t id_b = __builtin_amdgcn_readlane(my_id, i + 1);
+            const int32_t id_b = step_id(i + 1);
             load_page(id_b, kb, vb);
-            consume(id_a, (pc + i) * BS, ka, va);
-            consume(id_b, (pc + i + 1) * BS, kb, vb);
+            consume(id_a, (pc + i * VP) * BS, ka, va);
+            consume(id_b, (pc + (i + 1) * VP) * BS, kb, vb);
         } else {
-            consume(id_a, (pc + i) * BS, ka, va);
+            consume(id_a, (pc + i * VP) * BS, ka, va);
         }
     }
 
@@ -426,9 +447,18 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
 constexpr int64_t kTargetWorkgroups = 7 * 256;
 constexpr int64_t kMaxAutoParts = 64;
 
-inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size, int32_t batch,
-                              int32_t num_kv_heads, int32_t max_seqlen_k) {
-    if (partition_tokens > 0) return partition_tokens < block_size ? block_size : partition_tokens;
+// Keys per kernel step: a page, or for pages smaller than one 16-byte load per lane
+// (block size 2 or 4) the rows one load covers (bf16's count, a multiple of fp32's).
+inline int32_t step_keys(int32_t block_size, int32_t head_dim) {
+    return std::max(block_size, 1024 / std::max(head_dim * 2, 1));
+}
+
+inline int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
+
+inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size, int32_t head_dim,
+                              int32_t batch, int32_t num_kv_heads, int32_t max_seqlen_k) {
+    const int32_t granule = step_keys(block_size, head_dim);
+    if (partition_tokens > 0) return round_up(partition_tokens, granule);
     int per_wg = PA_DECODE_HPW;
     while (num_kv_heads % per_wg != 0) per_wg >>= 1;
     const int64_t groups = num_kv_heads / per_wg;
@@ -437,7 +467,7 @@ inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size, int3
     // about kMaxAutoParts partitions per sequence at most: the merge reads each one's state
     p = std::max<int64_t>(p, (static_cast<int64_t>(max_seqlen_k) / kMaxAutoParts + 32) / 64 * 64);
     p = std::max<int64_t>(128, std::min<int64_t>(4096, p));
-    return static_cast<int32_t>((p + block_size - 1) / block_size * block_size);
+    return round_up(static_cast<int32_t>(p), granule);
 }
 
 template <typename T, int D, int BS, int G>
@@ -504,6 +534,10 @@ int dispatch_shape(int G, const pa_kv_pool* pool, void* out, const void* q, int3
     PA_DECODE_SHAPE(128, 32)
     PA_DECODE_SHAPE(64, 8)
     PA_DECODE_SHAPE(128, 8)
+    PA_DECODE_SHAPE(64, 4)
+    PA_DECODE_SHAPE(128, 4)
+    PA_DECODE_SHAPE(64, 2)
+    PA_DECODE_SHAPE(128, 2)
 #undef PA_DECODE_SHAPE
     return PA_ERR_UNSUPPORTED;
 }
@@ -527,7 +561,8 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads,
     using namespace pa;
     if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
         return 0;
-    const int32_t p = pick_partition(partition_tokens, block_size, batch, num_kv_heads, max_seqlen_k);
+    const int32_t p = pick_partition(partition_tokens, block_size, head_dim, batch, num_kv_heads,
+                                     max_seqlen_k);
     return workspace_bytes(batch, num_heads, head_dim, num_parts(max_seqlen_k, p));
 }
 
@@ -551,8 +586,8 @@ int decode_impl(const pa_kv_pool* pool, void* out, const void* q, const void* k_
     if (pool->num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
     if (partition_tokens % pool->block_size != 0) return PA_ERR_INVALID_ARG;
     if (batch > 65535) return PA_ERR_UNSUPPORTED;
-    const int32_t part_tokens = pick_partition(partition_tokens, pool->block_size, batch,
-                                               pool->num_kv_heads, max_seqlen_k);
+    const int32_t part_tokens = pick_partition(partition_tokens, pool->block_size, pool->head_dim,
+                                               batch, pool->num_kv_heads, max_seqlen_k);
     if (part_tokens % pool->block_size != 0) return PA_ERR_INVALID_ARG;
     // keys beyond the table width are never read, so the width also bounds the grid
     const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * pool->block_size;
@@ -585,7 +620,8 @@ int prefill_by_token(const pa_kv_pool* pool, void* out, const void* q, int32_t b
                      int32_t max_seqlen_q, const int32_t* block_table, int32_t max_blocks,
                      float scale, int32_t causal, hipStream_t s) {
     if (pool->num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
-    const int32_t part_tokens = std::max(max_blocks, 1) * pool->block_size;  // one partition
+    const int32_t part_tokens =  // one partition
+        round_up(std::max(max_blocks, 1) * pool->block_size, step_keys(pool->block_size, pool->head_dim));
     const int G = num_heads / pool->num_kv_heads;
     const int64_t bound = static_cast<int64_t>(batch) * max_seqlen_q;  // tokens, at most
     for (int64_t first = 0; first < bound; first += 65535) {

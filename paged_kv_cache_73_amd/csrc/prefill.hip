@@ -619,9 +619,9 @@ extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* 
     if (out == nullptr || q == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
         (max_blocks_per_seq > 0 && block_table == nullptr))
         return PA_ERR_INVALID_ARG;
-    if (pool->block_size != 8 && pool->block_size != 16 && pool->block_size != 32)
-        return PA_ERR_UNSUPPORTED;
-    if (pool->dtype == PA_F32 || pool->block_size == 8) {  // not on the matrix-core kernel
+    const int32_t bs = pool->block_size;
+    if (bs != 2 && bs != 4 && bs != 8 && bs != 16 && bs != 32) return PA_ERR_UNSUPPORTED;
+    if (pool->dtype == PA_F32 || bs < 16) {  // not on the matrix-core kernel
         if (num_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
         if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;
         return prefill_by_token(pool, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,

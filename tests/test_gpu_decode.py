@@ -110,6 +110,18 @@ def test_decode_decode_table_example():
     assert g.plan.new_slots == [94, 32, 198]
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_decode_block_table_example_b4(head_dim):
+    # [NANO] 题目5: block table [3, 1, 5] with B = 4 puts token 9 in block 5 at offset 1.
+    # Ten keys (tokens 0..9), the tenth written through that slot, then one decode.
+    w = W.decode_workload([9], dtype="bf16", num_heads=4, num_kv_heads=2, head_dim=head_dim,
+                          block_size=4, num_blocks=8, max_blocks=3, seed=8)
+    w.order = [3, 1, 5, 0, 2, 4, 6, 7]
+    g, _ = _check_decode(w)
+    assert g.plan.tables == [[3, 1, 5]]
+    assert g.plan.new_slots == [5 * 4 + 1]
+
+
 SHAPES = [  # (dtype, Hq, Hkv, d, B)
     ("bf16", 16, 8, 128, 16),
     ("bf16", 8, 8, 128, 16),
@@ -123,6 +135,13 @@ SHAPES = [  # (dtype, Hq, Hkv, d, B)
     ("bf16", 8, 1, 64, 8),
     ("f32", 8, 4, 64, 8),
     ("f32", 4, 2, 128, 8),
+    # pages smaller than one 16-byte load per lane covers: each lane loads its own block
+    ("bf16", 16, 8, 128, 4),
+    ("bf16", 8, 2, 64, 4),
+    ("bf16", 16, 8, 128, 2),
+    ("bf16", 4, 1, 64, 2),
+    ("f32", 8, 4, 128, 2),
+    ("f32", 4, 2, 64, 2),
 ]
 
 
@@ -132,6 +151,7 @@ def test_decode_shapes(shape, partition_tokens):
     dtype, hq, hkv, d, B = shape
     if partition_tokens % B:
         pytest.skip("partition must be a multiple of B")
+    # (with pages of 2 or 4 tokens a partition rounds up to whole loads: 32 and 64 stay)
     rng = random.Random(hq * 1000 + d + B)
     cached = [0, 1, B - 1, B, 3 * B + 5, rng.randint(1, 700), rng.randint(1, 700), 599]
     w = W.decode_workload(cached, dtype=dtype, num_heads=hq, num_kv_heads=hkv, head_dim=d,
@@ -227,6 +247,8 @@ FUSED_CASES = [  # (cached lengths, dtype, Hq, Hkv, d, B, partition tokens)
     ([5, 63, 64, 700, 1023], "bf16", 16, 2, 64, 32, 64),
     ([3, 16, 40, 129], "f32", 8, 4, 128, 16, 16),
     ([0, 31, 32, 500], "f32", 4, 1, 64, 32, 0),
+    ([0, 1, 2, 3, 7, 70], "bf16", 8, 2, 64, 4, 0),
+    ([0, 1, 2, 9, 33], "bf16", 16, 8, 128, 2, 8),
 ]
 
 

@@ -157,7 +157,17 @@ F32_SHAPES = [  # (Hq, Hkv, d, B)
     (8, 8, 64, 16),
     (8, 1, 128, 32),
     (4, 2, 128, 8),
+    (8, 4, 128, 4),
+    (4, 2, 64, 2),
 ]
+
+
+@pytest.mark.parametrize("B", [2, 4])
+def test_prefill_bf16_small_blocks(B):
+    # pages of 2 or 4 tokens ([NANO] 题目5 and 题目6 use B = 4 and 2) take the token path
+    w = W.prefill_workload([0, 7, 31], [5, 19, 2], num_heads=16, num_kv_heads=8, head_dim=128,
+                           block_size=B, seed=46 + B)
+    _run(w)
 
 
 @pytest.mark.parametrize("causal", [True, False])
