@@ -143,14 +143,21 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     int32_t* const jobs = reinterpret_cast<int32_t*>(k_lds_all[1]);  // key tiles of each job
     __shared__ int32_t found;
     if (rank_requests) {
-        for (int j = tid; j < batch; j += kPrefillThreads) klen[j] = cu_k[j + 1] - cu_k[j];
+        const int padded = (batch + 3) & ~3;  // whole 16-byte reads; -1 pads (below any count)
+        for (int j = tid; j < padded; j += kPrefillThreads)
+            klen[j] = j < batch ? cu_k[j + 1] - cu_k[j] : -1;
         __syncthreads();
+        const int4* const klen4 = reinterpret_cast<const int4*>(klen);
         for (int j = tid; j < batch; j += kPrefillThreads) {
             const int kj = klen[j];
             int ahead = 0;  // requests before j in the order: longer, or as long and earlier
-            for (int i = 0; i < batch; ++i) {
-                const int ki = klen[i];
-                ahead += (ki > kj) | ((ki == kj) & (i < j));
+#pragma unroll 4
+            for (int i = 0; i < padded / 4; ++i) {
+                const int4 k4 = klen4[i];
+                ahead += (k4.x > kj) | ((k4.x == kj) & (4 * i + 0 < j));
+                ahead += (k4.y > kj) | ((k4.y == kj) & (4 * i + 1 < j));
+                ahead += (k4.z > kj) | ((k4.z == kj) & (4 * i + 2 < j));
+                ahead += (k4.w > kj) | ((k4.w == kj) & (4 * i + 3 < j));
             }
             perm[ahead] = j;
         }
@@ -159,18 +166,31 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     auto request_of = [&](int rank) { return rank_requests ? perm[rank] : rank; };
     int group, qtile;
     if (rank_jobs) {
-        // job c of this XCD: group (c / n_qtiles) * 8 + xcd, query tile c % n_qtiles
-        for (int c = tid; c < n_jobs; c += kPrefillThreads) {
-            const int g = (c / n_qtiles) * kXcds + xcd;
-            jobs[c] = g < n_groups ? job_tiles(request_of(g / num_kv_heads), (c % n_qtiles) * TOK) : -1;
+        // job c of this XCD: group (c / n_qtiles) * 8 + xcd, query tile c % n_qtiles.  Its
+        // sort key packs the key tiles (+1, so that -1 for "no job" stays non-negative)
+        // above 0xFFFF - c, so that keys are distinct and a larger key means "earlier":
+        // more tiles, or as many and a lower index.  The rank of job c is the number of
+        // larger keys; the table is padded with zeros (below every key) to whole 16-byte
+        // reads.
+        const int padded = (n_jobs + 3) & ~3;
+        for (int c = tid; c < padded; c += kPrefillThreads) {
+            int32_t key = 0;
+            if (c < n_jobs) {
+                const int g = (c / n_qtiles) * kXcds + xcd;
+                const int tiles = g < n_groups ? job_tiles(request_of(g / num_kv_heads), (c % n_qtiles) * TOK) : -1;
+                key = (min(tiles + 1, 0x7FFE) << 16) | (0xFFFF - c);
+            }
+            jobs[c] = key;
         }
         __syncthreads();
+        const int4* const jobs4 = reinterpret_cast<const int4*>(jobs);
         for (int c = tid; c < n_jobs; c += kPrefillThreads) {
-            const int v = jobs[c];
-            int ahead = 0;  // jobs before c: more tiles, or as many and a lower index
-            for (int i = 0; i < n_jobs; ++i) {
-                const int u = jobs[i];
-                ahead += (u > v) | ((u == v) & (i < c));
+            const int32_t v = jobs[c];
+            int ahead = 0;
+#pragma unroll 4
+            for (int i = 0; i < padded / 4; ++i) {
+                const int4 u = jobs4[i];
+                ahead += (u.x > v) + (u.y > v) + (u.z > v) + (u.w > v);
             }
             if (ahead == slot) found = c;
         }
