@@ -62,11 +62,11 @@ def write_bytes(w, plan) -> int:
 
 
 def prefill_flops(w, plan) -> float:
-    """4*d*Hq per visible (query, key) pair; causal pairs of request i with q_i queries
-    after c_i cached keys: q_i*c_i + q_i(q_i+1)/2."""
+    """4*d*Hq per visible (query, key) pair.  Request i with q_i queries after c_i cached
+    keys has q_i*c_i + q_i(q_i+1)/2 causal pairs, q_i*(c_i + q_i) without the mask."""
     tot = 0
     for qn, c in zip(w.new, w.cached):
-        tot += qn * c + qn * (qn + 1) // 2
+        tot += qn * c + (qn * (qn + 1) // 2 if w.causal else qn * qn)
     return 4.0 * w.head_dim * w.num_heads * tot
 
 
