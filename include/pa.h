@@ -39,8 +39,9 @@
  *   are not validated by the device calls (that would need a synchronisation);
  *   the pa_validate_* functions check host copies of them.
  * - Supported: dtype F32 or BF16, head_dim 64 or 128, block_size 2, 4, 8, 16 or 32,
- *   num_heads / num_kv_heads in {1, 2, 4, 8}, num_kv_heads <= 64.  Other shapes
- *   return PA_ERR_UNSUPPORTED.
+ *   num_heads / num_kv_heads in {1, 2, 4, 8}, num_kv_heads <= 64; head_dim 256 too for
+ *   the decode calls and the paged prefill, with block_size up to 16 (BF16) or 8 (F32).
+ *   Other shapes return PA_ERR_UNSUPPORTED.
  */
 #ifndef PA_H
 #define PA_H
@@ -189,9 +190,9 @@ int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q, const voi
  * cu_seqlens_k, scale, causal, block_table); [HFPA] Değişken uzunluklu yol).
  *
  * q, out: device, [total_q][num_heads][d] with total_q = cu_seqlens_q[batch], in the
- *   pool's dtype.  BF16 pools with block_size 16 or 32 run on the matrix cores; F32 pools
- *   and block_size 2, 4 or 8 run each query token as a decode query over its visible keys
- *   (no matrix cores, one partition per token).
+ *   pool's dtype.  BF16 pools with block_size 16 or 32 and head_dim 64 or 128 run on the
+ *   matrix cores; F32 pools, block_size 2, 4 or 8 and head_dim 256 run each query token as
+ *   a decode query over its visible keys (no matrix cores, one partition per token).
  * cu_seqlens_q, cu_seqlens_k: device int32 [batch+1], non-decreasing from 0.  Request
  *   i owns query rows [cu_q[i], cu_q[i+1]) and k_len = cu_k[i+1]-cu_k[i] keys, read
  *   through block_table row i (only the differences of cu_k are used; the new tokens'
@@ -202,8 +203,8 @@ int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q, const voi
  *   queries of a request beyond max_seqlen_q are not computed.
  * softmax_scale must be positive and finite (PA_ERR_INVALID_ARG otherwise).
  * Supported: BF16 or F32 pools, head_dim 64 or 128, block_size 2, 4, 8, 16 or 32, num_heads /
- *   num_kv_heads in {1, 2, 4, 8}, and on the token path num_kv_heads <= 64; otherwise
- *   PA_ERR_UNSUPPORTED.
+ *   num_kv_heads in {1, 2, 4, 8}, and on the token path num_kv_heads <= 64; head_dim 256
+ *   with block_size up to 16 (BF16) or 8 (F32); otherwise PA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------------- */
 int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                       int32_t num_heads, const int32_t* cu_seqlens_q,

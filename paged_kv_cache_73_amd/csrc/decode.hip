@@ -31,6 +31,7 @@
 //   invalid id is never loaded.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -538,6 +539,14 @@ int dispatch_shape(int G, const pa_kv_pool* pool, void* out, const void* q, int3
     PA_DECODE_SHAPE(128, 4)
     PA_DECODE_SHAPE(64, 2)
     PA_DECODE_SHAPE(128, 2)
+    // head_dim 256: pages of up to 16 rows in bf16 and 8 in fp32 (larger pages hold too
+    // many registers in the ping-pong buffers and spill)
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        PA_DECODE_SHAPE(256, 16)
+    }
+    PA_DECODE_SHAPE(256, 8)
+    PA_DECODE_SHAPE(256, 4)
+    PA_DECODE_SHAPE(256, 2)
 #undef PA_DECODE_SHAPE
     return PA_ERR_UNSUPPORTED;
 }

@@ -641,7 +641,7 @@ extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* 
         return PA_ERR_INVALID_ARG;
     const int32_t bs = pool->block_size;
     if (bs != 2 && bs != 4 && bs != 8 && bs != 16 && bs != 32) return PA_ERR_UNSUPPORTED;
-    if (pool->dtype == PA_F32 || bs < 16) {  // not on the matrix-core kernel
+    if (pool->dtype == PA_F32 || bs < 16 || pool->head_dim > 128) {  // not on the matrix cores
         if (num_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
         if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;
         return prefill_by_token(pool, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,

@@ -142,6 +142,12 @@ SHAPES = [  # (dtype, Hq, Hkv, d, B)
     ("bf16", 4, 1, 64, 2),
     ("f32", 8, 4, 128, 2),
     ("f32", 4, 2, 64, 2),
+    # head_dim 256 (bf16 pages up to 16 rows, fp32 up to 8)
+    ("bf16", 16, 8, 256, 16),
+    ("bf16", 8, 1, 256, 8),
+    ("bf16", 4, 2, 256, 2),
+    ("f32", 4, 2, 256, 8),
+    ("f32", 8, 4, 256, 4),
 ]
 
 
@@ -235,6 +241,21 @@ def test_decode_workspace_and_argument_errors():
         pa.pa_decode(g.pool, g.out[:, :12].contiguous(), g.q[:, :12].contiguous(), g.table,
                      g.seqlens, 701, w.scale, 0, small)
     assert e.value.code == -1
+
+
+@pytest.mark.parametrize("dtype,d,B", [("f32", 256, 16), ("bf16", 256, 32), ("bf16", 96, 16)])
+def test_decode_unsupported_shapes_are_refused(dtype, d, B):
+    # shapes outside the kernel tables return PA_ERR_UNSUPPORTED before any launch
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    kc = torch.zeros(4, B, 2, d, dtype=tdt, device="cuda")
+    pool = pa.KVPool(kc, torch.zeros_like(kc))
+    q = torch.zeros(1, 4, d, dtype=tdt, device="cuda")
+    out = torch.zeros_like(q)
+    table = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    seqlens = torch.ones(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode(pool, out, q, table, seqlens, 1, 0.1)
+    assert e.value.code == -2
 
 
 # --------------------------------------------------------------------------------------

@@ -159,7 +159,15 @@ F32_SHAPES = [  # (Hq, Hkv, d, B)
     (4, 2, 128, 8),
     (8, 4, 128, 4),
     (4, 2, 64, 2),
+    (4, 2, 256, 8),
 ]
+
+
+def test_prefill_bf16_head_dim_256():
+    # head_dim 256 runs on the token path (the matrix-core kernel takes 64 and 128)
+    w = W.prefill_workload([0, 20, 70], [9, 33, 4], num_heads=8, num_kv_heads=4, head_dim=256,
+                           block_size=16, seed=47)
+    _run(w)
 
 
 @pytest.mark.parametrize("B", [2, 4])
