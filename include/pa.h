@@ -220,9 +220,11 @@ int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t 
  *
  * k, v: device, [total_k][num_kv_heads][head_dim] with total_k = cu_seqlens_k[batch];
  *   request i's keys are rows [cu_k[i], cu_k[i+1]).  q, out: [total_q][num_heads]
- *   [head_dim] as for pa_prefill_varlen; dtype: PA_BF16 (PA_F32 returns
- *   PA_ERR_UNSUPPORTED).  Masking, alignment, scale and supported shapes as for
- *   pa_prefill_varlen.  Nothing is owned or kept by the library.
+ *   [head_dim] as for pa_prefill_varlen; dtype PA_BF16 or PA_F32.  BF16 with head_dim 64
+ *   or 128 runs on the matrix cores; F32 and head_dim 256 run each query token over its
+ *   request's rows (the token path of pa_prefill_varlen), reading no key past
+ *   max_seqlen_k.  Masking, alignment and scale as for pa_prefill_varlen; head_dim 64,
+ *   128 or 256.  Nothing is owned or kept by the library.
  * ------------------------------------------------------------------------------- */
 int pa_prefill_varlen_contiguous(void* out, const void* q, const void* k, const void* v,
                                  int32_t dtype, int32_t batch, int32_t num_heads,

@@ -98,7 +98,9 @@ constexpr int kPass1 = 1, kPass2 = 2;
 // "sequence" b is query token offset + blockIdx.z of the packed batch, its request is
 // the one whose [cu_q[i], cu_q[i+1]) holds it, and it attends to that request's first
 // k_len keys, or to keys j <= c + t when causal (c = k_len - q_len, t its index in the
-// request).  cu_q == nullptr: ordinary decode.
+// request).  cu_q == nullptr: ordinary decode.  With `contiguous`, the keys are packed
+// rows (no block table): the pool has one row per block, and key j of request i is
+// block cu_k[i] + j.
 struct TokenMap {
     const int32_t* cu_q = nullptr;
     const int32_t* cu_k = nullptr;
@@ -106,6 +108,7 @@ struct TokenMap {
     int32_t causal = 0;
     int32_t offset = 0;
     int32_t max_q = 0;  // tokens of a request past max_q are not computed
+    int32_t contiguous = 0;
 };
 
 #if PA_DECODE_WAVES_PER_EU > 0
@@ -141,6 +144,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     const int32_t cap = max_blocks * BS;
     int32_t n_keys;
     int64_t row_index = b;  // block-table row
+    int32_t first_block = 0;  // contiguous keys: the block (row) of key 0
     if (tm.cu_q != nullptr) {
         if (b >= tm.cu_q[tm.n_req]) return;  // past the packed tokens (uniform)
         int lo = 0, hi = tm.n_req;           // cu_q[lo] <= b < cu_q[hi]
@@ -154,6 +158,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
         if (t >= tm.max_q) return;
         n_keys = tm.causal ? min(k_len, k_len - q_len + t + 1) : k_len;
         row_index = lo;
+        if (tm.contiguous) first_block = tm.cu_k[lo];
     } else {
         n_keys = seqlens[b];
     }
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     // Fused append (k_new != null): the current token sits at position seqlen - 1.  The
     // workgroup of the last partition stores its K/V row in the cache and, when it
     // consumes that page, takes the row from registers rather than from memory.
-    const int32_t* table_row = block_table + row_index * max_blocks;
+    const int32_t* table_row = tm.contiguous ? nullptr : block_table + row_index * max_blocks;
     const bool appending = k_new != nullptr && seqlen > 0 && part == n_parts - 1;
     const int32_t new_pos = seqlen - 1;
     uint4 nk = make_uint4(0, 0, 0, 0), nv = make_uint4(0, 0, 0, 0);
@@ -306,7 +311,8 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     if (num_blocks <= 0) pg1 = pg0;  // nothing can be read
     for (int32_t pc = pg0; pc < pg1; pc += kWave) {
         const int np = (min(kWave, pg1 - pc) + VP - 1) / VP;  // (virtual) pages of the chunk
-        const int32_t my_id = (lane < min(kWave, pg1 - pc)) ? table_row[pc + lane] : -1;
+        const int32_t my_id = lane >= min(kWave, pg1 - pc) ? -1
+                              : tm.contiguous ? first_block + pc + lane : table_row[pc + lane];
         // id of step i: a scalar, or with small pages this lane's block
         auto step_id = [&](int i) -> int32_t {
             if constexpr (S::kSmall) return __shfl(my_id, i * VP + r0 / BS);
@@ -544,6 +550,10 @@ int dispatch_shape(int G, const pa_kv_pool* pool, void* out, const void* q, int3
     if constexpr (std::is_same<T, bf16_t>::value) {
         PA_DECODE_SHAPE(256, 16)
     }
+    // one row per block: packed contiguous keys on the token path (and pools of B = 1)
+    PA_DECODE_SHAPE(64, 1)
+    PA_DECODE_SHAPE(128, 1)
+    PA_DECODE_SHAPE(256, 1)
     PA_DECODE_SHAPE(256, 8)
     PA_DECODE_SHAPE(256, 4)
     PA_DECODE_SHAPE(256, 2)
@@ -595,6 +605,10 @@ int decode_impl(const pa_kv_pool* pool, void* out, const void* q, const void* k_
     if (pool->num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
     if (partition_tokens % pool->block_size != 0) return PA_ERR_INVALID_ARG;
     if (batch > 65535) return PA_ERR_UNSUPPORTED;
+    {   // block sizes of the public calls (one-row blocks serve packed keys internally)
+        const int32_t bs = pool->block_size;
+        if (bs != 2 && bs != 4 && bs != 8 && bs != 16 && bs != 32) return PA_ERR_UNSUPPORTED;
+    }
     const int32_t part_tokens = pick_partition(partition_tokens, pool->block_size, pool->head_dim,
                                                batch, pool->num_kv_heads, max_seqlen_k);
     if (part_tokens % pool->block_size != 0) return PA_ERR_INVALID_ARG;
@@ -627,7 +641,7 @@ int decode_impl(const pa_kv_pool* pool, void* out, const void* q, const void* k_
 int prefill_by_token(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                      int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
                      int32_t max_seqlen_q, const int32_t* block_table, int32_t max_blocks,
-                     float scale, int32_t causal, hipStream_t s) {
+                     float scale, int32_t causal, hipStream_t s, int32_t contiguous) {
     if (pool->num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
     const int32_t part_tokens =  // one partition
         round_up(std::max(max_blocks, 1) * pool->block_size, step_keys(pool->block_size, pool->head_dim));
@@ -642,6 +656,7 @@ int prefill_by_token(const pa_kv_pool* pool, void* out, const void* q, int32_t b
         tm.causal = causal != 0;
         tm.offset = static_cast<int32_t>(first);
         tm.max_q = max_seqlen_q;
+        tm.contiguous = contiguous;
         const int st = pool->dtype == PA_BF16
             ? dispatch_shape<bf16_t>(G, pool, out, q, n, num_heads, block_table, max_blocks,
                                      nullptr, nullptr, nullptr, 1, part_tokens, scale, nullptr,

@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 int prefill_by_token(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                      int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
                      int32_t max_seqlen_q, const int32_t* block_table, int32_t max_blocks,
-                     float scale, int32_t causal, hipStream_t s);
+                     float scale, int32_t causal, hipStream_t s, int32_t contiguous);
 
 // Where the keys live: a paged pool (table != null) or packed contiguous arrays.
 struct KvSource {
@@ -646,7 +646,7 @@ extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* 
         if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;
         return prefill_by_token(pool, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,
                                 max_seqlen_q, block_table, max_blocks_per_seq, softmax_scale,
-                                causal, static_cast<hipStream_t>(stream));
+                                causal, static_cast<hipStream_t>(stream), 0);
     }
     if (pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
     (void)max_seqlen_k;  // the per-request lengths bound the key loop
@@ -674,7 +674,17 @@ extern "C" int pa_prefill_varlen_contiguous(void* out, const void* q, const void
     if (out == nullptr || q == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
         (max_seqlen_k > 0 && (k == nullptr || v == nullptr)))
         return PA_ERR_INVALID_ARG;
-    if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (dtype != PA_BF16 || head_dim > 128) {
+        // fp32, or head_dim 256: the token path, the packed rows seen as a pool of one-row
+        // blocks in which key j of request i is block cu_k[i] + j (no table is read)
+        if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+        if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return PA_ERR_INVALID_ARG;
+        const pa_kv_pool rows{dtype, INT32_MAX, 1, num_kv_heads, head_dim, const_cast<void*>(k),
+                              const_cast<void*>(v)};
+        return prefill_by_token(&rows, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,
+                                max_seqlen_q, nullptr, std::max(max_seqlen_k, 1), softmax_scale,
+                                causal, static_cast<hipStream_t>(stream), 1);
+    }
     const KvSource kv{false, k, v, num_kv_heads, 0, 0, nullptr, 0};
     return prefill_impl(kv, head_dim, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,
                         max_seqlen_q, softmax_scale, causal, static_cast<hipStream_t>(stream));

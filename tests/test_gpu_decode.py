@@ -243,7 +243,8 @@ def test_decode_workspace_and_argument_errors():
     assert e.value.code == -1
 
 
-@pytest.mark.parametrize("dtype,d,B", [("f32", 256, 16), ("bf16", 256, 32), ("bf16", 96, 16)])
+@pytest.mark.parametrize("dtype,d,B", [("f32", 256, 16), ("bf16", 256, 32), ("bf16", 96, 16),
+                                       ("bf16", 128, 1), ("bf16", 128, 64)])
 def test_decode_unsupported_shapes_are_refused(dtype, d, B):
     # shapes outside the kernel tables return PA_ERR_UNSUPPORTED before any launch
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16

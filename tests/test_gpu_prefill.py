@@ -267,10 +267,11 @@ def test_chunked_prefill_full_size(seed):
 # contiguous (non-paged) K/V
 # --------------------------------------------------------------------------------------
 
-def _contiguous_case(w, requests=None):
+def _contiguous_case(w, requests=None, bitwise=True):
     """Run the paged step and the contiguous call on the same inputs; check the
-    contiguous output against the oracle and against the paged output (bit for bit:
-    the same tiles in the same order)."""
+    contiguous output against the oracle and, on the matrix-core kernel, against the
+    paged output (bit for bit: the same tiles in the same order).  On the token path
+    the two group keys differently (pages vs single rows), so only the oracle decides."""
     g = H.gpu_setup(w)
     H.gpu_step(w, g)
     k, v = W.contiguous_kv(w)
@@ -279,7 +280,8 @@ def _contiguous_case(w, requests=None):
     pa.pa_prefill_varlen_contiguous(out, g.q, kd, vd, g.cu_q, g.cu_k, g.plan.max_q, g.plan.max_k,
                                     w.scale, w.causal)
     torch.cuda.synchronize()
-    assert torch.equal(out, g.out)
+    if bitwise:
+        assert torch.equal(out, g.out)
     q = H.storage(w.q, w.dtype)
     ks, vs = H.storage(k, w.dtype), H.storage(v, w.dtype)
     cu_q, cu_k = g.plan.cu_q, g.plan.cu_k
@@ -291,6 +293,17 @@ def _contiguous_case(w, requests=None):
                                            [0, cu_k[i + 1] - cu_k[i]], w.scale, w.causal, w.dtype)
         H.assert_close(got[rq], ref, w.dtype, f"contiguous {w.name} request {i}")
     return out
+
+
+@pytest.mark.parametrize("case", [("f32", 4, 2, 64), ("f32", 8, 4, 128), ("f32", 4, 2, 256),
+                                  ("bf16", 8, 4, 256)], ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("causal", [True, False])
+def test_contiguous_prefill_token_path(case, causal):
+    # fp32 and head_dim 256: each packed query token attends its request's packed rows
+    dtype, hq, hkv, d = case
+    w = W.prefill_workload([0, 9, 40, 3], [7, 1, 25, 0], dtype=dtype, num_heads=hq,
+                           num_kv_heads=hkv, head_dim=d, block_size=8, causal=causal, seed=48)
+    _contiguous_case(w, bitwise=False)
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
@@ -325,16 +338,17 @@ def test_contiguous_prefill_edge_cases(golden):
     got = H.out_f64(out)
     H.assert_close(got, ref, "bf16", "varlen example, contiguous")
     assert not got[:12].any() and got[12].any() and got[13].any()
-    # batch 0 and max_seqlen_q 0 are no-ops; f32 is unsupported; bad scale is an error
+    # batch 0 and max_seqlen_q 0 are no-ops; head_dim 96 is unsupported; bad scale is an error
     out.fill_(7.0)
     pa.pa_prefill_varlen_contiguous(out[:0], q[:0].cuda(), k.cuda(), v.cuda(), tq[:1], tk[:1], 0, 0,
                                     0.3, True)
     pa.pa_prefill_varlen_contiguous(out, q.cuda(), k.cuda(), v.cuda(), tq, tk, 0, 7, 0.3, True)
     torch.cuda.synchronize()
     assert bool((out.float() == 7.0).all())
+    z = lambda n, h: torch.zeros((n, h, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(pa.PaError) as e:
-        pa.pa_prefill_varlen_contiguous(out.float(), q.float().cuda(), k.float().cuda(),
-                                        v.float().cuda(), tq, tk, 10, 7, 0.3, True)
+        pa.pa_prefill_varlen_contiguous(z(14, hq), z(14, hq), z(8, hkv), z(8, hkv), tq, tk, 10, 7,
+                                        0.3, True)
     assert e.value.code == -2
     with pytest.raises(pa.PaError) as e:
         pa.pa_prefill_varlen_contiguous(out, q.cuda(), k.cuda(), v.cuda(), tq, tk, 10, 7, 0.0, True)
