@@ -375,62 +375,105 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     const int32_t* __restrict__ seqlens, const float* __restrict__ o_part,
     const float* __restrict__ ml_part, T* __restrict__ out, int32_t num_heads, int32_t cap,
     int32_t max_parts, int32_t part_tokens) {
-    constexpr int PER = D / kWave;  // dims per lane
+    constexpr int PER = D / kWave;    // dims per lane
+    constexpr int CH = 32 / PER;      // partitions whose o rows are loaded together
     const int h = blockIdx.x;
     const int b = blockIdx.y;
     const int lane = threadIdx.x;
-    const int32_t seqlen = min(max(seqlens[b], 0), cap);
-    const int32_t n_parts = max(1, (seqlen + part_tokens - 1) / part_tokens);
-    if (n_parts == 1) return;  // finished by pass 1
     const int64_t bh = static_cast<int64_t>(b) * num_heads + h;
     const float2* ml = reinterpret_cast<const float2*>(ml_part) + bh * max_parts;
     const float* op = o_part + bh * max_parts * D;
 
-    // global maximum: lane p looks at partitions p, p+64, ...
-    float M = -INFINITY;
-    for (int p = lane; p < n_parts; p += kWave) M = fmaxf(M, ml[p].x);
+    // Loads that do not depend on the sequence length go out first, together with it: the
+    // (m, l) of partitions 0..63 and the o rows of the first CH partitions, at indices
+    // clamped to the workspace (entries past the sequence's partitions are never used:
+    // they are selected away, not multiplied, since the workspace there is uninitialised).
+    const int32_t seqlen_raw = seqlens[b];
+    const int last = max_parts - 1;
+    const float2 st = ml[min(lane, last)];
+    float v[CH][PER];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    for (int u = 0; u < CH; ++u)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) v[u][k] = op[min(u, last) * D + lane + k * kWave];
+    // keep the compiler from sinking these loads below the length test (it would wait for
+    // the length first and then for the loads: two trips to memory instead of one)
+    asm volatile("" ::"v"(st.x), "v"(st.y));
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) asm volatile("" ::"v"(v[u][k]));
+    const int32_t seqlen = min(max(seqlen_raw, 0), cap);
+    const int32_t n_parts = max(1, (seqlen + part_tokens - 1) / part_tokens);
+    if (n_parts == 1) return;  // finished by pass 1
 
-    // boxed merge with m_new = M for every partition at once
     float L = 0.f, O[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) O[k] = 0.f;
-    if (M != -INFINITY) {
-        for (int p0 = 0; p0 < n_parts; p0 += kWave) {
-            const int cnt = min(kWave, n_parts - p0);
-            float wl = 0.f, ll = 0.f;
-            if (lane < cnt) {
-                const float2 st = ml[p0 + lane];
-                wl = __builtin_amdgcn_exp2f(st.x - M);
-                ll = st.y;
-            }
-            L += wl * ll;
-            // four partitions per trip so that their loads are in flight together
-            int i = 0;
-            for (; i + 4 <= cnt; i += 4) {
-                float v[4][PER], wi[4];
+    if (n_parts <= kWave) {
+        // lane p holds partition p's state: global maximum, weights, l, then the o rows
+        // CH partitions at a time, the next CH in flight while the current ones are summed
+        const bool mine = lane < n_parts;
+        float M = mine ? st.x : -INFINITY;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    wi[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i + u));
-                    const float* src = op + static_cast<int64_t>(p0 + i + u) * D + lane;
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        if (M != -INFINITY) {
+            const float wl = mine ? __builtin_amdgcn_exp2f(st.x - M) : 0.f;
+            L = mine ? wl * st.y : 0.f;
+            for (int p0 = 0;; p0 += CH) {
+                const bool more = p0 + CH < n_parts;
+                float vn[CH][PER];
+                if (more) {
 #pragma unroll
-                    for (int k = 0; k < PER; ++k) v[u][k] = src[k * kWave];
+                    for (int u = 0; u < CH; ++u)
+#pragma unroll
+                        for (int k = 0; k < PER; ++k)
+                            vn[u][k] = op[min(p0 + CH + u, last) * D + lane + k * kWave];
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < CH; ++u) {
+                    if (p0 + u < n_parts) {
+                        const float w = __int_as_float(
+                            __builtin_amdgcn_readlane(__float_as_int(wl), p0 + u));
 #pragma unroll
-                    for (int k = 0; k < PER; ++k) O[k] += wi[u] * v[u][k];
-            }
-            for (; i < cnt; ++i) {
-                const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
-                const float* src = op + static_cast<int64_t>(p0 + i) * D + lane;
+                        for (int k = 0; k < PER; ++k) O[k] += w * v[u][k];
+                    }
+                }
+                if (!more) break;
 #pragma unroll
-                for (int k = 0; k < PER; ++k) O[k] += wi * src[k * kWave];
+                for (int u = 0; u < CH; ++u)
+#pragma unroll
+                    for (int k = 0; k < PER; ++k) v[u][k] = vn[u][k];
             }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
         }
+    } else {
+        // more partitions than lanes: global maximum, then 64 partitions' states at a time
+        float M = -INFINITY;
+        for (int p = lane; p < n_parts; p += kWave) M = fmaxf(M, ml[p].x);
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        if (M != -INFINITY) {
+            for (int p0 = 0; p0 < n_parts; p0 += kWave) {
+                const int cnt = min(kWave, n_parts - p0);
+                float wl = 0.f, ll = 0.f;
+                if (lane < cnt) {
+                    const float2 sp = ml[p0 + lane];
+                    wl = __builtin_amdgcn_exp2f(sp.x - M);
+                    ll = sp.y;
+                }
+                L += wl * ll;
+                for (int i = 0; i < cnt; ++i) {
+                    const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+                    const float* src = op + static_cast<int64_t>(p0 + i) * D + lane;
+#pragma unroll
+                    for (int k = 0; k < PER; ++k) O[k] += wi * src[k * kWave];
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+        }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
