@@ -70,20 +70,24 @@ def prefill_flops(w, plan) -> float:
     return 4.0 * w.head_dim * w.num_heads * tot
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    """First 16 hex digits of the SHA-256 of the files' bytes, concatenated in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_file: str, workload: str):
+def load_traffic(kernel_files, workload: str):
     """HBM traffic per launch from a committed rocprofv3 counter summary, if it was
-    taken on the current source of the kernel; otherwise None."""
+    taken on the current source of the kernel (and of its launch code); otherwise None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256_16") != source_hash(kernel_file):
+    if rec.get("source_sha256_16") != source_hash(kernel_files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -281,8 +285,9 @@ def main() -> int:
         del kc, vc
 
     plan = r.plan
-    kernel_src = os.path.join(ROOT, "paged_kv_cache_73_amd", "csrc",
-                              "decode.hip" if w.kind == "decode" else "prefill.hip")
+    csrc = os.path.join(ROOT, "paged_kv_cache_73_amd", "csrc")
+    kernel_src = ([os.path.join(csrc, "decode_kernel.h"), os.path.join(csrc, "decode.hip")]
+                  if w.kind == "decode" else [os.path.join(csrc, "prefill.hip")])
     cfg = {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
            "num_blocks": w.num_blocks, "seed": args.seed}

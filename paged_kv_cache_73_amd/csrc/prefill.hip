@@ -224,11 +224,14 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int row = w * 32 + r;   // row of the workgroup this lane owns
     const int tok = tok0 + row / G;
     const int head = hkv * G + row % G;
-    const bool row_ok = tok < q_len;
+    // with a group size that does not divide the rows (3, 5, 6, 7) the last rows past
+    // TOK whole tokens are idle: they would belong to the next workgroup's first token
+    constexpr bool kAllRows = TOK * G == kPrefillRows;
+    const bool row_ok = tok < q_len && (kAllRows || row < TOK * G);
     // last key each row may see (the causal limit and the request's end)
     const int row_limit = min(causal ? cached + tok : k_len - 1, kv_end - 1);
     const int wave_first = min(tok0 + (w * 32) / G, q_len - 1);
-    const int wave_last = min(tok0 + (w * 32 + 31) / G, q_len - 1);
+    const int wave_last = min(tok0 + (kAllRows ? w * 32 + 31 : min(w * 32 + 31, TOK * G - 1)) / G, q_len - 1);
     const int wave_lo = min(causal ? cached + wave_first : k_len - 1, kv_end - 1);  // all rows see keys <= this
     const int wave_hi = min(causal ? cached + wave_last : k_len - 1, kv_end - 1);   // no row sees keys > this
 
@@ -598,7 +601,11 @@ int dispatch_prefill_group(int G, const KvSource& kv, void* out, const void* q, 
     switch (G) {
         PA_PREFILL_CASE(1)
         PA_PREFILL_CASE(2)
+        PA_PREFILL_CASE(3)
         PA_PREFILL_CASE(4)
+        PA_PREFILL_CASE(5)
+        PA_PREFILL_CASE(6)
+        PA_PREFILL_CASE(7)
         PA_PREFILL_CASE(8)
         default: return PA_ERR_UNSUPPORTED;
     }

@@ -148,6 +148,12 @@ SHAPES = [  # (dtype, Hq, Hkv, d, B)
     ("bf16", 4, 2, 256, 2),
     ("f32", 4, 2, 256, 8),
     ("f32", 8, 4, 256, 4),
+    # GQA groups that are not powers of two (3, 5, 6, 7 query heads per KV head)
+    ("bf16", 6, 2, 128, 16),
+    ("bf16", 10, 2, 64, 32),
+    ("f32", 12, 2, 128, 16),
+    ("bf16", 28, 4, 128, 16),
+    ("f32", 7, 1, 64, 8),
 ]
 
 
@@ -243,14 +249,18 @@ def test_decode_workspace_and_argument_errors():
     assert e.value.code == -1
 
 
-@pytest.mark.parametrize("dtype,d,B", [("f32", 256, 16), ("bf16", 256, 32), ("bf16", 96, 16),
-                                       ("bf16", 128, 1), ("bf16", 128, 64)])
-def test_decode_unsupported_shapes_are_refused(dtype, d, B):
+@pytest.mark.parametrize("dtype,d,B,hq", [("f32", 256, 16, 4), ("bf16", 256, 32, 4),
+                                          ("bf16", 96, 16, 4), ("bf16", 128, 1, 4),
+                                          ("bf16", 128, 64, 4),
+                                          # group sizes 9 and 16; group 3 at d 256, 5 at B 4
+                                          ("bf16", 128, 16, 18), ("bf16", 128, 16, 32),
+                                          ("bf16", 256, 16, 6), ("f32", 64, 4, 10)])
+def test_decode_unsupported_shapes_are_refused(dtype, d, B, hq):
     # shapes outside the kernel tables return PA_ERR_UNSUPPORTED before any launch
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     kc = torch.zeros(4, B, 2, d, dtype=tdt, device="cuda")
     pool = pa.KVPool(kc, torch.zeros_like(kc))
-    q = torch.zeros(1, 4, d, dtype=tdt, device="cuda")
+    q = torch.zeros(1, hq, d, dtype=tdt, device="cuda")
     out = torch.zeros_like(q)
     table = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
     seqlens = torch.ones(1, dtype=torch.int32, device="cuda")
@@ -271,6 +281,7 @@ FUSED_CASES = [  # (cached lengths, dtype, Hq, Hkv, d, B, partition tokens)
     ([0, 31, 32, 500], "f32", 4, 1, 64, 32, 0),
     ([0, 1, 2, 3, 7, 70], "bf16", 8, 2, 64, 4, 0),
     ([0, 1, 2, 9, 33], "bf16", 16, 8, 128, 2, 8),
+    ([0, 1, 15, 16, 17, 300], "bf16", 28, 4, 128, 16, 0),
 ]
 
 

@@ -44,6 +44,11 @@ SHAPES = [  # (Hq, Hkv, d, B)
     (16, 4, 128, 32),
     (16, 2, 64, 16),
     (8, 1, 64, 32),
+    # GQA groups that are not powers of two: 128 rows hold 42, 25, 21 or 18 whole tokens
+    (6, 2, 128, 16),
+    (10, 2, 64, 32),
+    (12, 2, 128, 16),
+    (28, 4, 128, 32),
 ]
 
 
@@ -153,6 +158,8 @@ def test_prefill_argument_errors():
 
 F32_SHAPES = [  # (Hq, Hkv, d, B)
     (4, 2, 64, 32),
+    (12, 2, 128, 16),
+    (14, 2, 64, 8),
     (8, 4, 128, 16),
     (8, 8, 64, 16),
     (8, 1, 128, 32),
@@ -296,7 +303,8 @@ def _contiguous_case(w, requests=None, bitwise=True):
 
 
 @pytest.mark.parametrize("case", [("f32", 4, 2, 64), ("f32", 8, 4, 128), ("f32", 4, 2, 256),
-                                  ("bf16", 8, 4, 256)], ids=lambda c: "-".join(map(str, c)))
+                                  ("bf16", 8, 4, 256), ("f32", 12, 2, 128)],
+                         ids=lambda c: "-".join(map(str, c)))
 @pytest.mark.parametrize("causal", [True, False])
 def test_contiguous_prefill_token_path(case, causal):
     # fp32 and head_dim 256: each packed query token attends its request's packed rows
