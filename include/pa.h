@@ -39,11 +39,11 @@
  *   are not validated by the device calls (that would need a synchronisation);
  *   the pa_validate_* functions check host copies of them.
  * - Supported: dtype F32 or BF16, head_dim 64 or 128, block_size 2, 4, 8, 16 or 32,
- *   group size G = num_heads / num_kv_heads from 1 to 8, num_kv_heads <= 64; head_dim
- *   256 too for the decode calls and the paged prefill, with block_size up to 16 (BF16)
- *   or 8 (F32).  Group sizes 3, 5, 6 and 7 need head_dim 64 or 128 and block_size 8, 16
- *   or 32 wherever the decode kernel runs (decode calls, and the prefill's token path
- *   below).  Other shapes return PA_ERR_UNSUPPORTED.
+ *   group size G = num_heads / num_kv_heads from 1 to 8, 16 or 32, num_kv_heads <= 64;
+ *   head_dim 256 too for the decode calls and the paged prefill, with block_size up to 16
+ *   (BF16) or 8 (F32).  Group sizes 3, 5, 6, 7, 16 and 32 need head_dim 64 or 128 and
+ *   block_size 8, 16 or 32 wherever the decode kernel runs (decode calls, and the
+ *   prefill's token path below).  Other shapes return PA_ERR_UNSUPPORTED.
  */
 #ifndef PA_H
 #define PA_H
@@ -205,10 +205,10 @@ int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q, const voi
  *   queries of a request beyond max_seqlen_q are not computed.
  * softmax_scale must be positive and finite (PA_ERR_INVALID_ARG otherwise).
  * Supported: BF16 or F32 pools, head_dim 64 or 128, block_size 2, 4, 8, 16 or 32, group
- *   size num_heads / num_kv_heads from 1 to 8, and on the token path num_kv_heads <= 64;
- *   head_dim 256 with block_size up to 16 (BF16) or 8 (F32).  On the token path group
- *   sizes 3, 5, 6 and 7 need head_dim 64 or 128 and block_size 8 or more.  Otherwise
- *   PA_ERR_UNSUPPORTED.
+ *   size num_heads / num_kv_heads from 1 to 8, 16 or 32, and on the token path
+ *   num_kv_heads <= 64; head_dim 256 with block_size up to 16 (BF16) or 8 (F32).  On the
+ *   token path group sizes 3, 5, 6, 7, 16 and 32 need head_dim 64 or 128 and block_size 8
+ *   or more.  Otherwise PA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------------- */
 int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                       int32_t num_heads, const int32_t* cu_seqlens_q,

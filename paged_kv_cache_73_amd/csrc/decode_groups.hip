@@ -1,8 +1,9 @@
-// Paged decode for GQA group sizes 3, 5, 6 and 7 (query heads per KV head), which models
-// such as those with 28 query heads over 4 KV heads use.  The same kernel as for the
-// power-of-two groups (decode_kernel.h), instantiated here for head_dim 64 and 128 and
-// block sizes 8, 16 and 32, plus one-row blocks for packed keys on the token path.  Other
-// shapes with these group sizes return PA_ERR_UNSUPPORTED.
+// Paged decode for GQA group sizes 3, 5, 6 and 7 (query heads per KV head, as in models
+// with 28 query heads over 4 KV heads) and 16 and 32 (a group spread over two or four
+// waves of eight heads each).  The same kernel as for groups of 1, 2, 4 and 8
+// (decode_kernel.h), instantiated here for head_dim 64 and 128 and block sizes 8, 16 and
+// 32, plus one-row blocks for packed keys on the token path.  Other shapes with these
+// group sizes return PA_ERR_UNSUPPORTED.
 
 #include "decode_kernel.h"
 
@@ -13,7 +14,7 @@ int decode_odd_groups(int G, const pa_kv_pool* pool, void* out, const void* q, i
                       const int32_t* seqlens, const void* k_new, const void* v_new,
                       int32_t max_parts, int32_t part_tokens, float scale, float* o_part,
                       float* ml_part, hipStream_t stream, const TokenMap& tm, int passes) {
-    if (G != 3 && G != 5 && G != 6 && G != 7) return PA_ERR_UNSUPPORTED;
+    if (G != 3 && G != 5 && G != 6 && G != 7 && G != 16 && G != 32) return PA_ERR_UNSUPPORTED;
     const int D = pool->head_dim, BS = pool->block_size;
 #define PA_DECODE_ODD(TT, DD, BB)                                                            \
     if (D == DD && BS == BB)                                                                 \

@@ -118,7 +118,11 @@ struct TokenMap {
 #define PA_DECODE_ATTR
 #endif
 
-template <typename T, int D, int BS, int G>
+// G query heads per wave.  SPLIT > 1 spreads a KV head's group of G * SPLIT query heads
+// over SPLIT waves (groups of 16 and 32, whose queries and states would not fit one
+// wave's registers): each wave streams the KV head's pages for its own G heads, the
+// pages being read again from L2 by the other waves of the group.
+template <typename T, int D, int BS, int G, int SPLIT = 1>
 __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_partial_kernel(
     const T* __restrict__ q, char* k_cache, char* v_cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
@@ -136,7 +140,9 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
 
     const int lane = threadIdx.x % kWave;
     const int heads_per_wg = blockDim.x / kWave;
-    const int hkv = blockIdx.x * heads_per_wg + threadIdx.x / kWave;
+    const int vkv = blockIdx.x * heads_per_wg + threadIdx.x / kWave;  // wave of the grid
+    const int hkv = vkv / SPLIT;                  // its KV head
+    const int h0 = hkv * (G * SPLIT) + (vkv % SPLIT) * G;  // its first query head
     const int part = blockIdx.y;
     const int b = blockIdx.z + tm.offset;
     const int r0 = lane / LPR;  // first row of this lane within a load
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     float qv[G][E];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int h = hkv * G + g;
+        const int h = h0 + g;
         const uint4 w = *reinterpret_cast<const uint4*>(
             q + (static_cast<int64_t>(b) * num_heads + h) * D + c * E);
         widen(w, qv[g], T{});
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
         nk = *reinterpret_cast<const uint4*>(k_new + nrow);
         nv = *reinterpret_cast<const uint4*>(v_new + nrow);
         const int32_t id = table_row[new_pos / BS];
-        if (r0 == 0 && id >= 0 && id < num_blocks) {
+        if (r0 == 0 && id >= 0 && id < num_blocks && vkv % SPLIT == 0) {  // one wave of the group
             const int64_t off = ((static_cast<int64_t>(id) * BS + new_pos % BS) * num_kv_heads + hkv) *
                                     S::kRowBytes + c * 16;
             *reinterpret_cast<uint4*>(k_cache + off) = nk;
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int h = hkv * G + g;
+        const int h = h0 + g;
         const int64_t bh = static_cast<int64_t>(b) * num_heads + h;
         if (n_parts == 1) {
             float r[E];
@@ -488,17 +494,18 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     }
 }
 
-template <typename T, int D, int BS, int G>
+template <typename T, int D, int BS, int G, int SPLIT = 1>
 int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
                   int32_t num_heads, const int32_t* table, int32_t max_blocks,
                   const int32_t* seqlens, const void* k_new, const void* v_new, int32_t max_parts,
                   int32_t part_tokens, float scale, float* o_part, float* ml_part, hipStream_t stream,
                   const TokenMap& tm, int passes) {
     const int hkv = pool->num_kv_heads;
+    const int waves = hkv * SPLIT;  // one wave per KV head and split of its group
     int per_wg = PA_DECODE_HPW;
-    while (hkv % per_wg != 0) per_wg >>= 1;
-    const dim3 grid(hkv / per_wg, max_parts, batch);
-    if (passes & kPass1) hipLaunchKernelGGL((decode_partial_kernel<T, D, BS, G>), grid, dim3(per_wg * kWave), 0, stream,
+    while (waves % per_wg != 0) per_wg >>= 1;
+    const dim3 grid(waves / per_wg, max_parts, batch);
+    if (passes & kPass1) hipLaunchKernelGGL((decode_partial_kernel<T, D, BS, G, SPLIT>), grid, dim3(per_wg * kWave), 0, stream,
                        static_cast<const T*>(q), static_cast<char*>(pool->k_cache),
                        static_cast<char*>(pool->v_cache), table, seqlens,
                        static_cast<const T*>(k_new), static_cast<const T*>(v_new),
@@ -513,7 +520,7 @@ int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batc
     return launch_status();
 }
 
-// Group sizes 1, 2, 4 and 8 are instantiated in decode.hip, 3, 5, 6 and 7 in
+// Group sizes 1, 2, 4 and 8 are instantiated in decode.hip; 3, 5, 6, 7, 16 and 32 in
 // decode_groups.hip (for the shapes listed there), so the two compile in parallel.
 template <typename T, int D, int BS>
 int dispatch_group_pow2(int G, const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
@@ -552,6 +559,14 @@ int dispatch_group_odd(int G, const pa_kv_pool* pool, void* out, const void* q, 
         PA_DECODE_G(5)
         PA_DECODE_G(6)
         PA_DECODE_G(7)
+        case 16:
+            return launch_decode<T, D, BS, 8, 2>(pool, out, q, batch, num_heads, table, max_blocks,
+                                                 seqlens, k_new, v_new, max_parts, part_tokens,
+                                                 scale, o_part, ml_part, stream, tm, passes);
+        case 32:
+            return launch_decode<T, D, BS, 8, 4>(pool, out, q, batch, num_heads, table, max_blocks,
+                                                 seqlens, k_new, v_new, max_parts, part_tokens,
+                                                 scale, o_part, ml_part, stream, tm, passes);
         default: return PA_ERR_UNSUPPORTED;
     }
 #undef PA_DECODE_G

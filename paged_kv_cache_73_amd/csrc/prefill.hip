@@ -607,6 +607,8 @@ int dispatch_prefill_group(int G, const KvSource& kv, void* out, const void* q, 
         PA_PREFILL_CASE(6)
         PA_PREFILL_CASE(7)
         PA_PREFILL_CASE(8)
+        PA_PREFILL_CASE(16)
+        PA_PREFILL_CASE(32)
         default: return PA_ERR_UNSUPPORTED;
     }
 #undef PA_PREFILL_CASE

@@ -154,6 +154,10 @@ SHAPES = [  # (dtype, Hq, Hkv, d, B)
     ("f32", 12, 2, 128, 16),
     ("bf16", 28, 4, 128, 16),
     ("f32", 7, 1, 64, 8),
+    # groups of 16 and 32 query heads, spread over two and four waves
+    ("bf16", 32, 2, 128, 16),
+    ("f32", 16, 1, 64, 32),
+    ("bf16", 32, 1, 128, 8),
 ]
 
 
@@ -252,8 +256,9 @@ def test_decode_workspace_and_argument_errors():
 @pytest.mark.parametrize("dtype,d,B,hq", [("f32", 256, 16, 4), ("bf16", 256, 32, 4),
                                           ("bf16", 96, 16, 4), ("bf16", 128, 1, 4),
                                           ("bf16", 128, 64, 4),
-                                          # group sizes 9 and 16; group 3 at d 256, 5 at B 4
-                                          ("bf16", 128, 16, 18), ("bf16", 128, 16, 32),
+                                          # group sizes 9, 12 and 64; 3 at d 256, 5 at B 4
+                                          ("bf16", 128, 16, 18), ("bf16", 128, 16, 24),
+                                          ("bf16", 64, 16, 128),
                                           ("bf16", 256, 16, 6), ("f32", 64, 4, 10)])
 def test_decode_unsupported_shapes_are_refused(dtype, d, B, hq):
     # shapes outside the kernel tables return PA_ERR_UNSUPPORTED before any launch
@@ -282,6 +287,7 @@ FUSED_CASES = [  # (cached lengths, dtype, Hq, Hkv, d, B, partition tokens)
     ([0, 1, 2, 3, 7, 70], "bf16", 8, 2, 64, 4, 0),
     ([0, 1, 2, 9, 33], "bf16", 16, 8, 128, 2, 8),
     ([0, 1, 15, 16, 17, 300], "bf16", 28, 4, 128, 16, 0),
+    ([0, 1, 15, 16, 17, 300], "bf16", 32, 2, 128, 16, 0),
 ]
 
 

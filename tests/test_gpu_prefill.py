@@ -49,6 +49,9 @@ SHAPES = [  # (Hq, Hkv, d, B)
     (10, 2, 64, 32),
     (12, 2, 128, 16),
     (28, 4, 128, 32),
+    # groups of 16 and 32: 8 and 4 tokens per workgroup
+    (32, 2, 128, 16),
+    (32, 1, 64, 32),
 ]
 
 
@@ -160,6 +163,7 @@ F32_SHAPES = [  # (Hq, Hkv, d, B)
     (4, 2, 64, 32),
     (12, 2, 128, 16),
     (14, 2, 64, 8),
+    (16, 1, 128, 16),
     (8, 4, 128, 16),
     (8, 8, 64, 16),
     (8, 1, 128, 32),
