@@ -106,3 +106,29 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
         bad = err > bound
         assert not bad.any(), (f"{what}: {int(bad.sum())} elements out of tolerance, worst "
                                f"excess {float((err - bound).max()):.3e}")
+
+
+def score_ramp(w: W.Workload, per_key: float, seed: int = 0) -> None:
+    """Rewrites w's queries and keys so that every sequence's scores rise along its keys
+    by about ``per_key`` (natural-log units) per key: every query row becomes one fixed
+    direction u with |u|^2 = d, and key j of a sequence gets t_j * u added, t_j chosen so
+    that scale * t_j * d = per_key * j.  A steep ramp moves the running maximum in every
+    key tile and spreads the weights far past the float32 exponent range, so a kernel
+    that failed to rescale would overflow.  Shared-prefix workloads are not supported."""
+    assert w.groups is None
+    gen = torch.Generator().manual_seed(seed)
+    d = w.head_dim
+    u = torch.randn(d, generator=gen, dtype=torch.float64)
+    u = u / u.norm() * np.sqrt(d)
+    w.q = u.expand(w.q.shape).to(w.q.dtype).contiguous()
+    step = per_key / (w.scale * d)
+    k_ctx, k_new = w.k_ctx.double(), w.k_new.double()
+    c0 = n0 = 0
+    for c, n in zip(w.cached, w.new):
+        j_ctx = torch.arange(c, dtype=torch.float64)
+        j_new = torch.arange(c, c + n, dtype=torch.float64)
+        k_ctx[c0:c0 + c] += (step * j_ctx)[:, None, None] * u
+        k_new[n0:n0 + n] += (step * j_new)[:, None, None] * u
+        c0, n0 = c0 + c, n0 + n
+    w.k_ctx = k_ctx.to(w.k_ctx.dtype).contiguous()
+    w.k_new = k_new.to(w.k_new.dtype).contiguous()

@@ -195,6 +195,24 @@ def test_decode_partitions_agree_and_relabelling_is_bitwise():
     assert torch.equal(g1.out, g2.out)
 
 
+@pytest.mark.parametrize("dtype,per_key", [("bf16", 0.2), ("bf16", -0.2), ("f32", 0.05)])
+def test_decode_steep_score_ramp(dtype, per_key):
+    # scores rising or falling along each context: every partition has a different
+    # maximum, the merge combines states whose weights differ by up to e^±330
+    w = W.decode_workload([100, 700, 1650], dtype=dtype, num_heads=8, num_kv_heads=4,
+                          head_dim=128, block_size=16, seed=16)
+    H.score_ramp(w, per_key)
+    for p in (0, 64, 256):
+        _check_decode(w, p, what=f"ramp {per_key} P={p}")
+
+
+def test_decode_large_scores():
+    w = W.decode_workload([100, 700, 1650, 3000], dtype="bf16", seed=17)
+    w.q = (w.q.float() * 30).to(w.q.dtype)
+    for p in (0, 128):
+        _check_decode(w, p, what=f"q x30 P={p}")
+
+
 def test_decode_edge_cases():
     # a single key gives its value exactly (bf16 in, bf16 out)
     w = W.decode_workload([0, 0], dtype="bf16", seed=13)

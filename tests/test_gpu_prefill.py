@@ -67,6 +67,22 @@ def test_prefill_shapes(shape, causal):
     _run(w)
 
 
+@pytest.mark.parametrize("per_key", [0.2, -0.2])
+def test_prefill_steep_score_ramp(per_key):
+    # scores rising (or falling) by 0.2 per key: the running maximum moves in every key
+    # tile, and the weights of one row span e^±260, far past float32's exponent range
+    w = W.prefill_workload([0, 300, 1000], [200, 77, 130], seed=27)
+    H.score_ramp(w, per_key)
+    _run(w)
+
+
+def test_prefill_large_scores():
+    # queries scaled by 30: scores ~ N(0, 900), a peaked softmax whose maximum jumps
+    w = W.prefill_workload([0, 500, 64], [150, 90, 64], seed=28)
+    w.q = (w.q.float() * 30).to(w.q.dtype)
+    _run(w)
+
+
 def test_prefill_single_query_equals_decode():
     w = W.prefill_workload([30, 32, 70, 0, 500], [1, 1, 1, 1, 1], seed=22)
     g, o = _run(w)
