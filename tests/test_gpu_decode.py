@@ -428,6 +428,19 @@ def test_decode_long_context_split_k(partition_tokens):
     _check_decode(w, partition_tokens, rows=[0, 3, 7], what=f"long P={partition_tokens}")
 
 
+def test_decode_context_of_131071_tokens():
+    # past the long-context workload: 8192 pages of 16 in one table row, 64 partitions of
+    # 2048 keys (automatic) or 32 of 4096; one oracle run serves both
+    w = W.decode_workload([131070, 70000], dtype="bf16", num_heads=8, num_kv_heads=4,
+                          head_dim=128, block_size=16, seed=18)
+    g, o = _decode_case(w, 0)
+    H.assert_close(H.out_f64(g.out), o.out, w.dtype, "131071 keys, automatic partition")
+    g.out.zero_()
+    H.gpu_step(w, g, 4096)
+    torch.cuda.synchronize()
+    H.assert_close(H.out_f64(g.out), o.out, w.dtype, "131071 keys, P=4096")
+
+
 def test_decode_workspace_reuse_across_calls_and_shapes():
     # the workspace holds nothing between calls: any earlier contents are overwritten
     w = W.decode_workload([900, 40, 2100, 300], dtype="bf16", seed=16)

@@ -290,6 +290,30 @@ def test_chunked_prefill_full_size(seed):
     _run(w, requests=[0, 3, 7, 12, 15])
 
 
+def test_prefill_long_request_sampled_rows():
+    # one request of 5000 new tokens after 6000 cached ones (and a short one beside it):
+    # 79 query tiles of one group, key ranges up to 11000; the oracle computes sampled rows,
+    # each as a one-query request over the keys its row sees
+    w = W.prefill_workload([6000, 40], [5000, 3], num_heads=16, num_kv_heads=8, head_dim=128,
+                           block_size=16, seed=29)
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g)
+    torch.cuda.synchronize()
+    o = H.oracle_run(w, attention=False)
+    q = H.storage(w.q, w.dtype)
+    table = np.asarray(o.plan.tables)
+    got = H.out_f64(g.out)
+    rng = random.Random(5)
+    for t in [0, 1, 63, 64, 2047, 4998, 4999] + rng.sample(range(5000), 6):
+        ref = OA.prefill_varlen(q[t:t + 1], o.k_pool, o.v_pool, [0, 1], [0, 6000 + t + 1],
+                                table[0:1], w.scale, True, w.dtype)
+        H.assert_close(got[t:t + 1], ref, w.dtype, f"long request row {t}")
+    last = slice(5000, 5003)
+    ref = OA.prefill_varlen(q[last], o.k_pool, o.v_pool, [0, 3], [0, 43], table[1:2], w.scale,
+                            True, w.dtype)
+    H.assert_close(got[last], ref, w.dtype, "short request")
+
+
 # --------------------------------------------------------------------------------------
 # contiguous (non-paged) K/V
 # --------------------------------------------------------------------------------------
