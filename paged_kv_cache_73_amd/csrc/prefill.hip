@@ -61,7 +61,11 @@ constexpr int kPrefillThreads = 256;
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X
 constexpr float kRescaleSlack = 8.f; // weights stay below 2^8 between rescales
 constexpr int kMaxRankedRequests = 256;  // requests ordered by key count in-kernel
-constexpr int kMaxRankedJobs = 1024;     // jobs per XCD ordered by key tiles in-kernel
+// Jobs per XCD ordered by key tiles in-kernel.  Ranking costs O(jobs^2) LDS compares per
+// workgroup and separates the query tiles of a group (which then stop sharing K/V pages
+// in L2); past a few jobs per workgroup slot the batch order, which keeps a group's tiles
+// together, measured faster.
+constexpr int kMaxRankedJobs = 384;
 
 // Instruction order for a run of N products whose operands come from LDS: AHEAD reads
 // first, then each product followed by the next read, so that AHEAD reads stay in
