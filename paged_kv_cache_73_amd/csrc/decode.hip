@@ -11,10 +11,13 @@ namespace pa {
 // 256 on an MI355X: enough to keep every CU fed, few enough that each streams a long
 // run of pages and the merge stays small), assuming contexts average 60 % of the
 // maximum, and no shorter than max_seqlen_k / kMaxAutoParts (to 64 tokens) so that the
-// longest sequences are not cut into very many partitions.  Rounded to 64 tokens and
-// kept within [128, 4096].
+// longest sequences are not cut into very many partitions -- unless so few sequences and
+// KV-head groups that this would leave fewer than kMinWorkgroups workgroups (a single
+// long sequence gets up to 256 partitions, none below 256 tokens).  Rounded to 64
+// tokens and kept within [128, 4096].
 constexpr int64_t kTargetWorkgroups = 7 * 256;
 constexpr int64_t kMaxAutoParts = 64;
+constexpr int64_t kMinWorkgroups = 1024;
 
 // Keys per kernel step: a page, or for pages smaller than one 16-byte load per lane
 // (block size 2 or 4) the rows one load covers (bf16's count, a multiple of fp32's).
@@ -33,8 +36,11 @@ inline int32_t pick_partition(int32_t partition_tokens, int32_t block_size, int3
     const int64_t groups = num_kv_heads / per_wg;
     const int64_t est_keys = static_cast<int64_t>(batch) * max_seqlen_k * 6 / 10;
     int64_t p = (est_keys * groups / kTargetWorkgroups + 63) / 64 * 64;
-    // about kMaxAutoParts partitions per sequence at most: the merge reads each one's state
-    p = std::max<int64_t>(p, (static_cast<int64_t>(max_seqlen_k) / kMaxAutoParts + 32) / 64 * 64);
+    // a bounded number of partitions per sequence: the merge reads each one's state
+    const int64_t few = std::min<int64_t>(kMinWorkgroups / std::max<int64_t>(1, batch * groups),
+                                          max_seqlen_k / 256);
+    const int64_t max_auto_parts = std::max<int64_t>(kMaxAutoParts, few);
+    p = std::max<int64_t>(p, (static_cast<int64_t>(max_seqlen_k) / max_auto_parts + 32) / 64 * 64);
     p = std::max<int64_t>(128, std::min<int64_t>(4096, p));
     return round_up(static_cast<int32_t>(p), granule);
 }

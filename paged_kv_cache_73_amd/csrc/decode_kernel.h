@@ -172,7 +172,8 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     const int32_t seqlen = min(max(n_keys, 0), cap);
     const int32_t part_tokens = part_pages * BS;
     const int32_t n_parts = max(1, (seqlen + part_tokens - 1) / part_tokens);
-    if (part >= n_parts) return;  // uniform over the workgroup
+    // uniform over the workgroup; the grid may hold one row past max_parts (odd row count)
+    if (part >= n_parts || part >= max_parts) return;
     const int32_t t_end = min(seqlen, (part + 1) * part_tokens);
     const int32_t pg0 = part * part_pages;
     int32_t pg1 = (t_end + BS - 1) / BS;
@@ -417,70 +418,52 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     float L = 0.f, O[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) O[k] = 0.f;
-    if (n_parts <= kWave) {
-        // lane p holds partition p's state: global maximum, weights, l, then the o rows
-        // CH partitions at a time, the next CH in flight while the current ones are summed
-        const bool mine = lane < n_parts;
-        float M = mine ? st.x : -INFINITY;
+    // Lane p of block b holds the state of partition 64b + p.  The global maximum first;
+    // then per block of 64 partitions the weights and l, and the o rows CH partitions at
+    // a time, the next CH (the next block's first ones at a block's end) in flight while
+    // the current ones are summed.  Partitions are summed in order.
+    float M = lane < n_parts ? st.x : -INFINITY;
+    for (int p = lane + kWave; p < n_parts; p += kWave) M = fmaxf(M, ml[p].x);
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-        if (M != -INFINITY) {
-            const float wl = mine ? __builtin_amdgcn_exp2f(st.x - M) : 0.f;
-            L = mine ? wl * st.y : 0.f;
-            for (int p0 = 0;; p0 += CH) {
-                const bool more = p0 + CH < n_parts;
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (M != -INFINITY) {
+        for (int p0 = 0; p0 < n_parts; p0 += kWave) {
+            const int cnt = min(kWave, n_parts - p0);
+            const bool mine = lane < cnt;
+            const float2 sp = p0 == 0 ? st : ml[min(p0 + lane, last)];
+            const float wl = mine ? __builtin_amdgcn_exp2f(sp.x - M) : 0.f;
+            L += mine ? wl * sp.y : 0.f;
+            for (int c0 = 0;; c0 += CH) {
+                const int nx = c0 + CH < cnt ? p0 + c0 + CH : p0 + kWave;  // next chunk
+                const bool more = nx < n_parts;
                 float vn[CH][PER];
                 if (more) {
 #pragma unroll
                     for (int u = 0; u < CH; ++u)
 #pragma unroll
                         for (int k = 0; k < PER; ++k)
-                            vn[u][k] = op[min(p0 + CH + u, last) * D + lane + k * kWave];
+                            vn[u][k] = op[min(nx + u, last) * D + lane + k * kWave];
                 }
 #pragma unroll
                 for (int u = 0; u < CH; ++u) {
-                    if (p0 + u < n_parts) {
+                    if (c0 + u < cnt) {
                         const float w = __int_as_float(
-                            __builtin_amdgcn_readlane(__float_as_int(wl), p0 + u));
+                            __builtin_amdgcn_readlane(__float_as_int(wl), c0 + u));
 #pragma unroll
                         for (int k = 0; k < PER; ++k) O[k] += w * v[u][k];
                     }
                 }
-                if (!more) break;
+                if (more) {
 #pragma unroll
-                for (int u = 0; u < CH; ++u)
+                    for (int u = 0; u < CH; ++u)
 #pragma unroll
-                    for (int k = 0; k < PER; ++k) v[u][k] = vn[u][k];
-            }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-        }
-    } else {
-        // more partitions than lanes: global maximum, then 64 partitions' states at a time
-        float M = -INFINITY;
-        for (int p = lane; p < n_parts; p += kWave) M = fmaxf(M, ml[p].x);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-        if (M != -INFINITY) {
-            for (int p0 = 0; p0 < n_parts; p0 += kWave) {
-                const int cnt = min(kWave, n_parts - p0);
-                float wl = 0.f, ll = 0.f;
-                if (lane < cnt) {
-                    const float2 sp = ml[p0 + lane];
-                    wl = __builtin_amdgcn_exp2f(sp.x - M);
-                    ll = sp.y;
+                        for (int k = 0; k < PER; ++k) v[u][k] = vn[u][k];
                 }
-                L += wl * ll;
-                for (int i = 0; i < cnt; ++i) {
-                    const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
-                    const float* src = op + static_cast<int64_t>(p0 + i) * D + lane;
-#pragma unroll
-                    for (int k = 0; k < PER; ++k) O[k] += wi * src[k * kWave];
-                }
+                if (c0 + CH >= cnt) break;
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
         }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
@@ -504,7 +487,12 @@ int launch_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batc
     const int waves = hkv * SPLIT;  // one wave per KV head and split of its group
     int per_wg = PA_DECODE_HPW;
     while (waves % per_wg != 0) per_wg >>= 1;
-    const dim3 grid(waves / per_wg, max_parts, batch);
+    // Workgroups go to the 8 XCDs round-robin in launch order.  With an even number of
+    // partition rows, partition p of every sequence would land on the same XCDs (those of
+    // p's parity), and the XCDs holding the later, partial or absent partitions would run
+    // short of work; an odd row count (an empty row added) rotates the assignment from one
+    // sequence to the next.
+    const dim3 grid(waves / per_wg, max_parts | 1, batch);
     if (passes & kPass1) hipLaunchKernelGGL((decode_partial_kernel<T, D, BS, G, SPLIT>), grid, dim3(per_wg * kWave), 0, stream,
                        static_cast<const T*>(q), static_cast<char*>(pool->k_cache),
                        static_cast<char*>(pool->v_cache), table, seqlens,
