@@ -218,6 +218,47 @@ int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t 
                       void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Varlen prefill with key splitting: pa_prefill_varlen's result (the same masking,
+ * alignment, shapes and errors) for batches with few query tiles.  On the matrix cores
+ * a job (one request, KV head and tile of 128 query rows) walks all its keys in one
+ * workgroup; when a batch has fewer jobs than the GPU has workgroup slots (a single long
+ * prompt's chunk, a few requests with one query head per KV head), jobs are cut into
+ * key ranges of at least 1024 keys processed by separate workgroups, each keeping the
+ * online-softmax state (m, l, o) of its range ([PA11] §11.2), and a second kernel folds
+ * the ranges with the §11.2 rule.  Results agree with pa_prefill_varlen within rounding
+ * (bit-identical when nothing is split).
+ *
+ * host_cu_seqlens_q, host_cu_seqlens_k: optional HOST copies of the two cu_seqlens
+ *   arrays (both or neither; NULL: plan from the bounds alone).  With them the split is
+ *   planned from every job's key count (about one key range per workgroup slot); without
+ *   them from max_seqlen_q and max_seqlen_k (for batches of mixed lengths the ranges are
+ *   then longer than they need be).  Either way max_seqlen_q and max_seqlen_k must bound
+ *   the requests' lengths; a request past max_seqlen_k still has all its keys attended
+ *   (its last range takes the rest).
+ * workspace: device scratch of at least pa_prefill_workspace_bytes(pool dtype, batch,
+ *   num_heads, num_kv_heads, head_dim, block_size, max_seqlen_q, max_seqlen_k, causal,
+ *   host_cu_seqlens_q, host_cu_seqlens_k) bytes, queried on the device the call runs on
+ *   (the plan counts its CUs); NULL when that is 0: the batch has enough jobs, or the
+ *   shape runs token by token.  Contents need no initialisation and are meaningless after
+ *   the call; calls sharing a workspace must not overlap.
+ * Errors: as pa_prefill_varlen, and PA_ERR_WORKSPACE when the workspace is missing or
+ *   too small.
+ * ------------------------------------------------------------------------------- */
+size_t pa_prefill_workspace_bytes(int32_t dtype, int32_t batch, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal,
+                                  const int32_t* host_cu_seqlens_q,
+                                  const int32_t* host_cu_seqlens_k);
+
+int pa_prefill_varlen_splitk(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                             int32_t num_heads, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                             int32_t max_seqlen_k, const int32_t* block_table,
+                             int32_t max_blocks_per_seq, float softmax_scale, int32_t causal,
+                             const int32_t* host_cu_seqlens_q, const int32_t* host_cu_seqlens_k,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Varlen prefill over contiguous (non-paged) K/V ([QWEN] fast-attn 库的使用: the same
  * varlen call without block_table, k and v then being packed like q; [HFPA]
  * Değişken uzunluklu yol).  The choice when nothing is cached yet.

@@ -30,6 +30,7 @@ EXPORTS = [
     "pa_validate_decode", "pa_validate_varlen", "pa_validate_slots", "pa_probe_stream_read",
     "pa_prefix_block_hash", "pa_bm_allocate_prefix", "pa_decode_append",
     "pa_prefill_varlen_contiguous", "pa_decode_partials", "pa_decode_merge",
+    "pa_prefill_workspace_bytes", "pa_prefill_varlen_splitk",
 ]
 
 
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
                                            _I32, _VP, ctypes.c_size_t, _VP]),
         "pa_prefill_varlen": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP, _VP,
                                              _I32, _I32, _VP, _I32, ctypes.c_float, _I32, _VP]),
+        "pa_prefill_workspace_bytes": (ctypes.c_size_t, [_I32] * 9 + [_I32P, _I32P]),
+        "pa_prefill_varlen_splitk": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP,
+                                                    _VP, _I32, _I32, _VP, _I32, ctypes.c_float, _I32,
+                                                    _I32P, _I32P, _VP, ctypes.c_size_t, _VP]),
         "pa_prefill_varlen_contiguous": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
                                                         _I32, _VP, _VP, _I32, _I32, ctypes.c_float,
                                                         _I32, _VP]),
@@ -299,6 +304,44 @@ def pa_prefill_varlen(pool: KVPool, out, q, cu_seqlens_q, cu_seqlens_k, max_seql
                                  _stream(stream))
     if st:
         _raise(st, "pa_prefill_varlen")
+
+
+def _host_i32(a):
+    """A host int32 array for an optional host-side copy of metadata (None stays None)."""
+    if a is None:
+        return None
+    arr = (ctypes.c_int32 * len(a))(*[int(x) for x in a])
+    return arr
+
+
+def pa_prefill_workspace_bytes(dtype: int, batch: int, num_heads: int, num_kv_heads: int,
+                               head_dim: int, block_size: int, max_seqlen_q: int,
+                               max_seqlen_k: int, causal: bool = True, host_cu_seqlens_q=None,
+                               host_cu_seqlens_k=None) -> int:
+    """Workspace of pa_prefill_varlen_splitk; host_cu_seqlens_q/k: optional host lists."""
+    return int(lib().pa_prefill_workspace_bytes(int(dtype), int(batch), int(num_heads),
+                                                int(num_kv_heads), int(head_dim), int(block_size),
+                                                int(max_seqlen_q), int(max_seqlen_k),
+                                                int(bool(causal)), _host_i32(host_cu_seqlens_q),
+                                                _host_i32(host_cu_seqlens_k)))
+
+
+def pa_prefill_varlen_splitk(pool: KVPool, out, q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                             max_seqlen_k: int, block_table, softmax_scale: float,
+                             causal: bool = True, workspace=None, host_cu_seqlens_q=None,
+                             host_cu_seqlens_k=None, stream=None) -> None:
+    batch = int(cu_seqlens_q.shape[0]) - 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pa_prefill_varlen_splitk(ctypes.byref(pool.struct), _dev(out, "out"), _dev(q, "q"),
+                                        batch, int(q.shape[1]), _meta(cu_seqlens_q, "cu_seqlens_q"),
+                                        _meta(cu_seqlens_k, "cu_seqlens_k"), int(max_seqlen_q),
+                                        int(max_seqlen_k), _meta(block_table, "block_table"),
+                                        int(block_table.shape[1]), float(softmax_scale),
+                                        int(bool(causal)), _host_i32(host_cu_seqlens_q),
+                                        _host_i32(host_cu_seqlens_k), _dev(workspace, "workspace"),
+                                        ws_bytes, _stream(stream))
+    if st:
+        _raise(st, "pa_prefill_varlen_splitk")
 
 
 def pa_prefill_varlen_contiguous(out, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,

@@ -70,6 +70,14 @@ constexpr int kMaxRankedJobs = 384;
 // Instruction order for a run of N products whose operands come from LDS: AHEAD reads
 // first, then each product followed by the next read, so that AHEAD reads stay in
 // flight (the scheduler otherwise moves every read next to its product).
+// Key ranges of a job of `tiles` key tiles when jobs are cut into ranges of split_tiles
+// tiles, at most n_split of them (the last one takes the rest).
+__host__ __device__ inline int split_count(int tiles, int n_split, int split_tiles) {
+    if (n_split <= 1 || tiles <= split_tiles) return 1;
+    const int parts = (tiles + split_tiles - 1) / split_tiles;
+    return parts < n_split ? parts : n_split;
+}
+
 template <int N, int AHEAD>
 __device__ __forceinline__ void pipeline_order() {
     constexpr int kLdsRead = 0x100, kMfma = 0x008;
@@ -87,7 +95,9 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const char* __restrict__ v_cache, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, const int32_t* __restrict__ block_table,
     uint16_t* __restrict__ out, int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks,
-    int32_t max_blocks, float qscale, int32_t causal, int32_t n_qtiles, int32_t n_groups) {
+    int32_t max_blocks, float qscale, int32_t causal, int32_t n_qtiles, int32_t n_groups,
+    int32_t n_split, int32_t split_tiles, float* __restrict__ part_o,
+    float2* __restrict__ part_ml) {
     constexpr int BN = kPrefillKeys;
     constexpr bool kPaged = BS > 0;
     constexpr int PBS = kPaged ? BS : BN;        // keys per page (one page per tile when contiguous)
@@ -129,7 +139,8 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int slot = L / kXcds;
     const int tid = threadIdx.x;
     const int batch = n_groups / num_kv_heads;
-    const int n_jobs = (n_groups + kXcds - 1) / kXcds * n_qtiles;  // workgroups per XCD
+    // work units per XCD: jobs, each cut into n_split key ranges when splitting
+    const int n_jobs = (n_groups + kXcds - 1) / kXcds * n_qtiles * n_split;
     // key tiles of a job: -1 when its first token is past the request's queries
     auto job_tiles = [&](int req, int tok0) {
         const int q_len = cu_q[req + 1] - cu_q[req];
@@ -139,6 +150,13 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         const int tok_last = min(tok0 + TOK, q_len) - 1;
         const int kv_end = causal ? min(k_len, k_len_req - q_len + tok_last + 1) : k_len;
         return (kv_end > 0 && (!kPaged || num_blocks > 0)) ? (kv_end + BN - 1) / BN : 0;
+    };
+    // key tiles of split s of a job with `tiles` tiles: -1 when the job has no such split
+    auto unit_tiles = [&](int tiles, int s) {
+        if (n_split == 1 || tiles < 0) return tiles;
+        const int parts = split_count(tiles, n_split, split_tiles);
+        if (s >= parts) return -1;
+        return parts == 1 ? tiles : (s == parts - 1 ? tiles - s * split_tiles : split_tiles);
     };
     const bool rank_requests = batch > 1 && batch <= kMaxRankedRequests;
     const bool rank_jobs = n_jobs > 1 && n_jobs <= kMaxRankedJobs;
@@ -168,7 +186,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         __syncthreads();
     }
     auto request_of = [&](int rank) { return rank_requests ? perm[rank] : rank; };
-    int group, qtile;
+    int group, qtile, split;
     if (rank_jobs) {
         // job c of this XCD: group (c / n_qtiles) * 8 + xcd, query tile c % n_qtiles.  Its
         // sort key packs the key tiles (+1, so that -1 for "no job" stays non-negative)
@@ -180,9 +198,11 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         for (int c = tid; c < padded; c += kPrefillThreads) {
             int32_t key = 0;
             if (c < n_jobs) {
-                const int g = (c / n_qtiles) * kXcds + xcd;
-                const int tiles = g < n_groups ? job_tiles(request_of(g / num_kv_heads), (c % n_qtiles) * TOK) : -1;
-                key = (min(tiles + 1, 0x7FFE) << 16) | (0xFFFF - c);
+                const int job = c / n_split;
+                const int g = (job / n_qtiles) * kXcds + xcd;
+                const int tiles = g < n_groups ? job_tiles(request_of(g / num_kv_heads), (job % n_qtiles) * TOK) : -1;
+                const int ut = unit_tiles(tiles, c % n_split);
+                key = (min(ut + 1, 0x7FFE) << 16) | (0xFFFF - c);
             }
             jobs[c] = key;
         }
@@ -200,13 +220,18 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         }
         __syncthreads();
         const int c = __builtin_amdgcn_readfirstlane(found);
-        group = (c / n_qtiles) * kXcds + xcd;
-        qtile = c % n_qtiles;
+        const int job = c / n_split;
+        group = (job / n_qtiles) * kXcds + xcd;
+        qtile = job % n_qtiles;
+        split = c % n_split;
     } else {
         // the groups of the XCD in turn, the query tiles of a group back to back, the
-        // later ones (which see more keys under the causal mask) first
-        group = (slot / n_qtiles) * kXcds + xcd;
-        qtile = n_qtiles - 1 - slot % n_qtiles;
+        // later ones (which see more keys under the causal mask) first, the key ranges
+        // of a job next to each other
+        const int job = slot / n_split;
+        group = (job / n_qtiles) * kXcds + xcd;
+        qtile = n_qtiles - 1 - job % n_qtiles;
+        split = slot % n_split;
     }
     if (group >= n_groups) return;  // uniform: grid padding
     const int hkv = group % num_kv_heads;
@@ -221,6 +246,11 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int tok_last = min(tok0 + TOK, q_len) - 1;
     const int kv_end = causal ? min(k_len, cached + tok_last + 1) : k_len;
     const int n_tiles = (kv_end > 0 && (!kPaged || num_blocks > 0)) ? (kv_end + BN - 1) / BN : 0;
+    // this unit's key tiles [t_lo, t_hi): the whole job, or one of its key ranges
+    const int n_split_job = n_split == 1 ? 1 : split_count(n_tiles, n_split, split_tiles);
+    if (split >= n_split_job) return;  // uniform: the job has no such key range
+    const int t_lo = split * split_tiles;  // 0 when the job is not split
+    const int t_hi = split == n_split_job - 1 ? n_tiles : t_lo + split_tiles;
     const int lane = tid % kWave;
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave index, kept in a scalar
     const int h = lane / 32;      // which 8-wide half of a 16-wide k-step this lane feeds
@@ -345,11 +375,11 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // ids of tile t + 1 are loaded during tile t - 1 and used during tile t
     u32x4 ids_next = u32x4{0, 0, 0, 0};
     uint32_t ok_cur = 0;
-    if (n_tiles > 0) {
-        const TileIds first = scalar_ids(0, load_ids(0));
-        fetch(0, first.wave);
+    if (t_hi > t_lo) {
+        const TileIds first = scalar_ids(t_lo, load_ids(t_lo));
+        fetch(t_lo, first.wave);
         ok_cur = first.bits;
-        if (n_tiles > 1) ids_next = load_ids(1);
+        if (t_hi - t_lo > 1) ids_next = load_ids(t_lo + 1);
     }
     // registers -> LDS buffer b for the tile whose loads are in kr / vr
     auto stage = [&](int b) {
@@ -509,28 +539,28 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // one barrier per tile: tile t + 1 is staged into the other buffer after tile t
     // is computed, while the loads of tile t + 2 are issued
     uint32_t ok_pend = 0;
-    if (n_tiles > 0) {
+    if (t_hi > t_lo) {
         __syncthreads();  // the orders staged in the K tile buffers are no longer read
         stage(0);
-        if (n_tiles > 1) {
-            const TileIds next = scalar_ids(1, ids_next);
-            fetch(1, next.wave);
+        if (t_hi - t_lo > 1) {
+            const TileIds next = scalar_ids(t_lo + 1, ids_next);
+            fetch(t_lo + 1, next.wave);
             ok_pend = next.bits;
-            if (n_tiles > 2) ids_next = load_ids(2);
+            if (t_hi - t_lo > 2) ids_next = load_ids(t_lo + 2);
         }
         __syncthreads();
     }
-    for (int t = 0; t < n_tiles; ++t) {
-        const int b = t & 1;
+    for (int t = t_lo; t < t_hi; ++t) {
+        const int b = (t - t_lo) & 1;
         if (t * BN <= wave_hi) compute(t, b, ok_cur);
-        if (t + 1 < n_tiles) {
+        if (t + 1 < t_hi) {
             stage(b ^ 1);
             ok_cur = ok_pend;
-            if (t + 2 < n_tiles) {
+            if (t + 2 < t_hi) {
                 const TileIds next = scalar_ids(t + 2, ids_next);
                 fetch(t + 2, next.wave);
                 ok_pend = next.bits;
-                if (t + 3 < n_tiles) ids_next = load_ids(t + 3);
+                if (t + 3 < t_hi) ids_next = load_ids(t + 3);
             }
         }
         __syncthreads();
@@ -538,6 +568,22 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 
     // normalise and store: lane holds d = 32db + 8i + 4h + jj of its row
     const float lt = l + __shfl_xor(l, 32);
+    if (n_split_job > 1) {
+        // one key range of a split job: the unnormalised O, the reference max m and l
+        // of each row go to the workspace, for prefill_merge_kernel
+        if (!row_ok) return;
+        const int64_t unit =
+            ((static_cast<int64_t>(req) * num_kv_heads + hkv) * n_qtiles + qtile) * n_split + split;
+        float* prow = part_o + (unit * kPrefillRows + row) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                *reinterpret_cast<float4*>(prow + 32 * db + 8 * i4 + 4 * h) =
+                    make_float4(acc[db][4 * i4], acc[db][4 * i4 + 1], acc[db][4 * i4 + 2], acc[db][4 * i4 + 3]);
+        if (h == 0) part_ml[unit * kPrefillRows + row] = make_float2(m, lt);
+        return;
+    }
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (!row_ok) return;
     uint16_t* orow = out + (static_cast<int64_t>(q0 + tok) * num_heads + head) * D;
@@ -551,6 +597,86 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                           (static_cast<uint32_t>(to_bf16_bits(acc[db][4 * i4 + 3] * inv)) << 16);
             *reinterpret_cast<uint2*>(orow + 32 * db + 8 * i4 + 4 * h) = make_uint2(lo, hi);
         }
+}
+
+// Second pass of a key-split prefill: for each row of a split job, the key ranges'
+// states (m_s, l_s, O_s) are folded with the online-softmax merge ("Paged attention 与
+// online softmax" §11.2: M = max m_s, O = sum 2^(m_s - M) O_s, l = sum 2^(m_s - M) l_s,
+// in base 2 as the states are) and O / l is stored.  Jobs are indexed (request, KV head,
+// query tile); jobs that were not split were finished by the first pass and are skipped.
+// A workgroup takes kMergeRows rows of a job, a thread 4 dims of one row, and the
+// ranges' loads are issued four at a time.
+constexpr int kMergeThreads = 256;
+
+template <int D, int G, int BS>
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    uint16_t* __restrict__ out, int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks,
+    int32_t max_blocks, int32_t causal, int32_t n_qtiles, int32_t n_split, int32_t split_tiles,
+    const float* __restrict__ part_o, const float2* __restrict__ part_ml) {
+    constexpr int BN = kPrefillKeys;
+    constexpr bool kPaged = BS > 0;
+    constexpr int TOK = kPrefillRows / G;
+    constexpr int D4 = D / 4;
+    constexpr int kMergeRows = kMergeThreads / D4;       // rows per workgroup
+    constexpr int kChunks = kPrefillRows / kMergeRows;  // workgroups per job
+    const int64_t job = blockIdx.x / kChunks;
+    const int row = (blockIdx.x % kChunks) * kMergeRows + threadIdx.x / D4;
+    const int d4 = threadIdx.x % D4;
+    const int qtile = static_cast<int>(job % n_qtiles);
+    const int hkv = static_cast<int>((job / n_qtiles) % num_kv_heads);
+    const int req = static_cast<int>(job / n_qtiles / num_kv_heads);
+    const int q0 = cu_q[req];
+    const int q_len = cu_q[req + 1] - q0;
+    const int tok0 = qtile * TOK;
+    const int tok = tok0 + row / G;
+    if (tok >= q_len || row >= TOK * G) return;  // past the request, or an idle row
+    // the first pass's key-tile count of this job, and so its number of key ranges
+    const int k_len_req = cu_k[req + 1] - cu_k[req];
+    const int k_len = kPaged ? min(k_len_req, max_blocks * BS) : k_len_req;
+    const int tok_last = min(tok0 + TOK, q_len) - 1;
+    const int kv_end = causal ? min(k_len, k_len_req - q_len + tok_last + 1) : k_len;
+    const int n_tiles = (kv_end > 0 && (!kPaged || num_blocks > 0)) ? (kv_end + BN - 1) / BN : 0;
+    const int parts = split_count(n_tiles, n_split, split_tiles);
+    if (parts <= 1) return;
+    const int64_t base = job * n_split * kPrefillRows + row;  // (range 0, this row)
+    const float2* ml = part_ml + base;
+    const float4* po = reinterpret_cast<const float4*>(part_o) + base * D4 + d4;
+    float M = -INFINITY;
+    for (int sp = 0; sp < parts; ++sp) M = fmaxf(M, ml[static_cast<int64_t>(sp) * kPrefillRows].x);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+    if (M != -INFINITY) {
+        for (int sp0 = 0; sp0 < parts; sp0 += 4) {
+            float2 st[4];
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t sp = min(sp0 + u, parts - 1);  // in range; the extra ones unused
+                st[u] = ml[sp * kPrefillRows];
+                v[u] = po[sp * kPrefillRows * D4];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (sp0 + u < parts) {
+                    const float wgt = __builtin_amdgcn_exp2f(st[u].x - M);  // 0: empty range
+                    L += wgt * st[u].y;
+                    o.x += wgt * v[u].x;
+                    o.y += wgt * v[u].y;
+                    o.z += wgt * v[u].z;
+                    o.w += wgt * v[u].w;
+                }
+            }
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int head = hkv * G + row % G;
+    uint16_t* orow = out + (static_cast<int64_t>(q0 + tok) * num_heads + head) * D + 4 * d4;
+    const uint32_t lo = static_cast<uint32_t>(to_bf16_bits(o.x * inv)) |
+                        (static_cast<uint32_t>(to_bf16_bits(o.y * inv)) << 16);
+    const uint32_t hi = static_cast<uint32_t>(to_bf16_bits(o.z * inv)) |
+                        (static_cast<uint32_t>(to_bf16_bits(o.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
 }
 
 // The varlen prefill run token by token on the decode kernel (decode.hip): the path
@@ -572,22 +698,119 @@ struct KvSource {
     int32_t max_blocks;   // paged only
 };
 
+// Key splitting (pa_prefill_varlen_splitk).  A job walks all its key tiles in one
+// workgroup, so when a batch has fewer jobs than the GPU has workgroup slots (two per CU),
+// the longest jobs alone set the time while most slots idle.  Such batches have their
+// jobs cut into key ranges, and a merge pass folds the ranges.  With the lengths on the
+// host and at most half as many jobs as slots (a chunk of one long prompt, a few
+// requests), ranges of about (all jobs' tiles) / slots tiles, at least
+// kMinSplitTilesExact, leave about one range per slot.  Otherwise (or with only the
+// bounds max_seqlen_q and max_seqlen_k) ranges of at least kMinSplitTiles tiles aim at
+// kSplitTargetUnits ranges for jobs of the longest length: mixed lengths then split
+// only their longest jobs, since every extra range adds its partial state (128 rows x
+// (d + 2) floats written, then read by the merge) and a workgroup's fixed costs.  The
+// plan depends only on the host arguments, so the workspace query and the call agree.
+constexpr int64_t kSplitBelowJobs = 1024;  // a bound on the jobs from which none is split
+constexpr int64_t kSplitTargetUnits = 1024;
+constexpr int64_t kMinSplitTiles = 16;
+constexpr int64_t kMinSplitTilesExact = 8;
+
+struct SplitPlan {
+    int32_t n_split;      // key ranges per job at most (1: no split)
+    int32_t split_tiles;  // key tiles per range (the last range of a job takes the rest)
+    int64_t units;        // dense jobs x n_split: rows of the workspace
+};
+
+// workgroup slots of the current device: two per CU (the prefill kernel's occupancy)
+inline int64_t prefill_slots() {
+    static int64_t slots = 0;
+    if (slots == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        slots = 2 * static_cast<int64_t>(cus);
+    }
+    return slots;
+}
+
+inline SplitPlan plan_split(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, bool causal,
+                            const int32_t* host_cu_q, const int32_t* host_cu_k) {
+    SplitPlan p{1, 0, 0};
+    if (batch <= 0 || num_kv_heads <= 0 || num_heads < num_kv_heads) return p;
+    const int64_t tok = std::max(kPrefillRows / (num_heads / num_kv_heads), 1);
+    const int64_t n_qtiles = (max_seqlen_q + tok - 1) / tok;
+    const int64_t dense = static_cast<int64_t>(batch) * num_kv_heads * n_qtiles;
+    if (dense == 0) return p;
+    int64_t st = 0, longest = 0;
+    if (host_cu_q != nullptr && host_cu_k != nullptr) {
+        // every job's key tiles, as the kernel counts them (without the table-width cap)
+        int64_t jobs = 0, tiles = 0;
+        for (int32_t i = 0; i < batch; ++i) {
+            const int64_t q_len = host_cu_q[i + 1] - host_cu_q[i];
+            const int64_t k_len = host_cu_k[i + 1] - host_cu_k[i];
+            for (int64_t t0 = 0; t0 < std::min<int64_t>(q_len, max_seqlen_q); t0 += tok) {
+                const int64_t last = std::min(t0 + tok, q_len) - 1;
+                const int64_t kv_end = causal ? std::min(k_len, k_len - q_len + last + 1) : k_len;
+                const int64_t t = kv_end > 0 ? (kv_end + kPrefillKeys - 1) / kPrefillKeys : 0;
+                jobs += num_kv_heads;
+                tiles += t * num_kv_heads;
+                longest = std::max(longest, t);
+            }
+        }
+        if (jobs == 0 || jobs >= prefill_slots()) return p;
+        if (2 * jobs <= prefill_slots())
+            st = std::max<int64_t>(kMinSplitTilesExact, (tiles + prefill_slots() - 1) / prefill_slots());
+    }
+    if (st == 0) {
+        longest = std::max(longest, (static_cast<int64_t>(max_seqlen_k) + kPrefillKeys - 1) / kPrefillKeys);
+        if (dense >= kSplitBelowJobs) return p;
+        st = std::max<int64_t>(kMinSplitTiles, (longest * dense + kSplitTargetUnits - 1) / kSplitTargetUnits);
+    }
+    if (longest <= st) return p;
+    p.n_split = static_cast<int32_t>((longest + st - 1) / st);
+    p.split_tiles = static_cast<int32_t>(st);
+    p.units = dense * p.n_split;
+    return p;
+}
+
+inline size_t split_workspace_bytes(const SplitPlan& p, int32_t head_dim) {
+    if (p.n_split <= 1) return 0;
+    return static_cast<size_t>(p.units) * kPrefillRows * (static_cast<size_t>(head_dim) * 4 + 8);
+}
+
 template <int D, int G, int BS>
 int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                    int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
-                   int32_t max_seqlen_q, float scale, int32_t causal, hipStream_t stream) {
+                   int32_t max_seqlen_q, float scale, int32_t causal, hipStream_t stream,
+                   const SplitPlan& sp, void* workspace) {
     const int tok_per_wg = kPrefillRows / G;
     const int64_t n_qtiles = (max_seqlen_q + tok_per_wg - 1) / tok_per_wg;
     const int64_t n_groups = static_cast<int64_t>(kv.num_kv_heads) * batch;
-    const int64_t padded = (n_groups + kXcds - 1) / kXcds * n_qtiles * kXcds;
+    const int64_t padded = (n_groups + kXcds - 1) / kXcds * n_qtiles * sp.n_split * kXcds;
     if (padded > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    float* part_o = sp.n_split > 1 ? static_cast<float*>(workspace) : nullptr;
+    float2* part_ml = sp.n_split > 1
+        ? reinterpret_cast<float2*>(part_o + static_cast<size_t>(sp.units) * kPrefillRows * D) : nullptr;
     const dim3 grid(static_cast<uint32_t>(padded));
     hipLaunchKernelGGL((prefill_kernel<D, G, BS>), grid, dim3(kPrefillThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const char*>(kv.k),
                        static_cast<const char*>(kv.v), cu_q, cu_k, kv.table,
                        static_cast<uint16_t*>(out), num_heads, kv.num_kv_heads,
                        kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
-                       static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups));
+                       static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups),
+                       sp.n_split, sp.split_tiles, part_o, part_ml);
+    if (sp.n_split > 1) {
+        if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+        const int64_t chunks = kPrefillRows / (kMergeThreads / (D / 4));  // workgroups per job
+        hipLaunchKernelGGL((prefill_merge_kernel<D, G, BS>), dim3(static_cast<uint32_t>(n_groups * n_qtiles * chunks)),
+                           dim3(kMergeThreads), 0, stream, cu_q, cu_k, static_cast<uint16_t*>(out),
+                           num_heads, kv.num_kv_heads, kv.num_blocks, kv.max_blocks, causal,
+                           static_cast<int32_t>(n_qtiles), sp.n_split, sp.split_tiles,
+                           static_cast<const float*>(part_o), static_cast<const float2*>(part_ml));
+    }
     return launch_status();
 }
 
@@ -595,9 +818,9 @@ template <int D>
 int dispatch_prefill_group(int G, const KvSource& kv, void* out, const void* q, int32_t batch,
                            int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
                            int32_t max_seqlen_q, float scale, int32_t causal,
-                           hipStream_t stream) {
+                           hipStream_t stream, const SplitPlan& sp, void* workspace) {
 #define PA_PREFILL_LAUNCH(GG, BB) \
-    launch_prefill<D, GG, BB>(kv, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, scale, causal, stream)
+    launch_prefill<D, GG, BB>(kv, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, scale, causal, stream, sp, workspace)
 #define PA_PREFILL_CASE(GG)                                                                     \
     case GG:                                                                                    \
         if (!kv.paged) return PA_PREFILL_LAUNCH(GG, 0);                              \
@@ -621,28 +844,36 @@ int dispatch_prefill_group(int G, const KvSource& kv, void* out, const void* q, 
 
 int prefill_impl(const KvSource& kv, int32_t head_dim, void* out, const void* q, int32_t batch,
                  int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
-                 int32_t max_seqlen_q, float scale, int32_t causal, hipStream_t s) {
+                 int32_t max_seqlen_q, float scale, int32_t causal, hipStream_t s,
+                 const SplitPlan& sp = SplitPlan{1, 0, 0}, void* workspace = nullptr) {
     if (num_heads % kv.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
     if (!(scale > 0.f) || scale == INFINITY) return PA_ERR_INVALID_ARG;
     const int G = num_heads / kv.num_kv_heads;
     if (head_dim == 128)
         return dispatch_prefill_group<128>(G, kv, out, q, batch, num_heads, cu_q, cu_k,
-                                           max_seqlen_q, scale, causal != 0, s);
+                                           max_seqlen_q, scale, causal != 0, s, sp, workspace);
     if (head_dim == 64)
         return dispatch_prefill_group<64>(G, kv, out, q, batch, num_heads, cu_q, cu_k,
-                                          max_seqlen_q, scale, causal != 0, s);
+                                          max_seqlen_q, scale, causal != 0, s, sp, workspace);
     return PA_ERR_UNSUPPORTED;
 }
 
 }  // namespace pa
 
-extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
-                                 int32_t num_heads, const int32_t* cu_seqlens_q,
-                                 const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
-                                 int32_t max_seqlen_k, const int32_t* block_table,
-                                 int32_t max_blocks_per_seq, float softmax_scale, int32_t causal,
-                                 void* stream) {
-    using namespace pa;
+namespace pa {
+
+// the paged pool's calls take the matrix cores for BF16 pools of head_dim <= 128 with
+// blocks of 16 or 32 rows; the rest runs token by token
+inline bool on_matrix_cores(int32_t dtype, int32_t block_size, int32_t head_dim) {
+    return dtype == PA_BF16 && block_size >= 16 && head_dim <= 128;
+}
+
+int paged_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                  int32_t num_heads, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int32_t max_seqlen_q, int32_t max_seqlen_k, const int32_t* block_table,
+                  int32_t max_blocks_per_seq, float softmax_scale, int32_t causal, void* stream,
+                  bool may_split, const int32_t* host_cu_q, const int32_t* host_cu_k,
+                  void* workspace, size_t workspace_bytes) {
     int st = check_pool(pool);
     if (st != PA_OK) return st;
     if (batch < 0 || num_heads <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
@@ -662,13 +893,67 @@ extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* 
                                 causal, static_cast<hipStream_t>(stream), 0);
     }
     if (pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
-    (void)max_seqlen_k;  // the per-request lengths bound the key loop
+    // without splitting the per-request lengths alone bound the key loop; the split plan
+    // reads max_seqlen_k (ranges past it would not be walked: a caller error)
+    SplitPlan sp{1, 0, 0};
+    if (may_split) {
+        sp = plan_split(batch, num_heads, pool->num_kv_heads, max_seqlen_q, max_seqlen_k,
+                        causal != 0, host_cu_q, host_cu_k);
+        const size_t need = split_workspace_bytes(sp, pool->head_dim);
+        if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    }
     // a table of width 0 (possibly null) assigns no block: every row outputs zeros, and
     // the kernel reads no table entry because no request then has a key to load
     const KvSource kv{true, pool->k_cache, pool->v_cache, pool->num_kv_heads, pool->num_blocks,
                       pool->block_size, block_table, max_blocks_per_seq};
     return prefill_impl(kv, pool->head_dim, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,
-                        max_seqlen_q, softmax_scale, causal, static_cast<hipStream_t>(stream));
+                        max_seqlen_q, softmax_scale, causal, static_cast<hipStream_t>(stream), sp,
+                        workspace);
+}
+
+}  // namespace pa
+
+extern "C" int pa_prefill_varlen(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                                 int32_t num_heads, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                                 int32_t max_seqlen_k, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, float softmax_scale, int32_t causal,
+                                 void* stream) {
+    return pa::paged_prefill(pool, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,
+                             max_seqlen_q, max_seqlen_k, block_table, max_blocks_per_seq,
+                             softmax_scale, causal, stream, false, nullptr, nullptr, nullptr, 0);
+}
+
+extern "C" size_t pa_prefill_workspace_bytes(int32_t dtype, int32_t batch, int32_t num_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_seqlen_q,
+                                             int32_t max_seqlen_k, int32_t causal,
+                                             const int32_t* host_cu_seqlens_q,
+                                             const int32_t* host_cu_seqlens_k) {
+    using namespace pa;
+    if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seqlen_q <= 0 ||
+        max_seqlen_k < 0 || num_heads % num_kv_heads != 0)
+        return 0;
+    if (!on_matrix_cores(dtype, block_size, head_dim)) return 0;
+    return split_workspace_bytes(plan_split(batch, num_heads, num_kv_heads, max_seqlen_q,
+                                            max_seqlen_k, causal != 0, host_cu_seqlens_q,
+                                            host_cu_seqlens_k),
+                                 head_dim);
+}
+
+extern "C" int pa_prefill_varlen_splitk(const pa_kv_pool* pool, void* out, const void* q,
+                                        int32_t batch, int32_t num_heads,
+                                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                        int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                                        float softmax_scale, int32_t causal,
+                                        const int32_t* host_cu_seqlens_q,
+                                        const int32_t* host_cu_seqlens_k, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    return pa::paged_prefill(pool, out, q, batch, num_heads, cu_seqlens_q, cu_seqlens_k,
+                             max_seqlen_q, max_seqlen_k, block_table, max_blocks_per_seq,
+                             softmax_scale, causal, stream, true, host_cu_seqlens_q,
+                             host_cu_seqlens_k, workspace, workspace_bytes);
 }
 
 extern "C" int pa_prefill_varlen_contiguous(void* out, const void* q, const void* k,

@@ -315,6 +315,101 @@ def test_prefill_long_request_sampled_rows():
 
 
 # --------------------------------------------------------------------------------------
+# key-split prefill (few jobs: key ranges in separate workgroups, then a merge)
+# --------------------------------------------------------------------------------------
+
+SPLIT_CASES = [  # (cached, new, Hq, Hkv, d, B, causal)
+    ([3000], [256], 16, 8, 128, 16, True),                   # a chunk of one long prompt
+    ([2000, 500, 4000], [300, 20, 100], 8, 8, 128, 16, True),  # one query head per KV head
+    ([2500, 100], [64, 200], 16, 8, 64, 32, False),
+    ([5000, 0], [100, 1], 28, 4, 128, 16, True),             # group of 7, a one-token request
+    ([1100], [1], 32, 2, 128, 16, True),                     # group of 16, one query token
+]
+
+
+def _splitk(w, g, workspace=None, need=None, exact=False):
+    """pa_prefill_varlen_splitk planned from the bounds, or (exact) from host copies of
+    the cu_seqlens arrays."""
+    from paged_kv_cache_73_amd._native import PA_BF16
+    hq, hk = (g.plan.cu_q, g.plan.cu_k) if exact else (None, None)
+    if need is None:
+        need = pa.pa_prefill_workspace_bytes(PA_BF16, w.batch, w.num_heads, w.num_kv_heads,
+                                             w.head_dim, w.block_size, g.plan.max_q, g.plan.max_k,
+                                             w.causal, hq, hk)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.full_like(g.out, 7.0)
+    pa.pa_prefill_varlen_splitk(g.pool, out, g.q, g.cu_q, g.cu_k, g.plan.max_q, g.plan.max_k,
+                                g.table, w.scale, w.causal, workspace, hq, hk)
+    torch.cuda.synchronize()
+    return out, need
+
+
+@pytest.mark.parametrize("exact", [False, True], ids=["bounds", "lengths"])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: f"{c[2]}-{c[3]}-{c[4]}-{c[5]}-{len(c[0])}req")
+def test_prefill_splitk_matches_oracle(case, exact):
+    cached, new, hq, hkv, d, B, causal = case
+    w = W.prefill_workload(cached, new, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                           block_size=B, causal=causal, seed=33)
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g)            # the unsplit prefill, for comparison
+    torch.cuda.synchronize()
+    out, need = _splitk(w, g, exact=exact)
+    assert need > 0             # these batches are split
+    o = H.oracle_run(w, attention=False)
+    q = H.storage(w.q, w.dtype)
+    table = np.asarray(o.plan.tables)
+    got = H.out_f64(out)
+    for i in range(w.batch):
+        rows = slice(o.plan.cu_q[i], o.plan.cu_q[i + 1])
+        ref = OA.prefill_varlen(q[rows], o.k_pool, o.v_pool, [0, rows.stop - rows.start],
+                                [0, o.plan.cu_k[i + 1] - o.plan.cu_k[i]], table[i:i + 1], w.scale,
+                                causal, w.dtype)
+        H.assert_close(got[rows], ref, w.dtype, f"split request {i}")
+    H.assert_close(got, H.out_f64(g.out), w.dtype, "split vs unsplit")
+    # the workspace needs no initialisation
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out2, _ = _splitk(w, g, ws, exact=exact)
+    assert torch.equal(out2, out)
+
+
+def test_prefill_splitk_without_split_is_the_plain_call():
+    # enough jobs: no split, no workspace, the same bits as pa_prefill_varlen
+    w = W.chunked_prefill(seed=1)
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g)
+    torch.cuda.synchronize()
+    for exact in (False, True):
+        out, need = _splitk(w, g, exact=exact)
+        assert need == 0
+        assert torch.equal(out, g.out)
+
+
+def test_prefill_splitk_masks_unassigned_blocks_and_checks_the_workspace():
+    w = W.prefill_workload([2000], [100], num_heads=8, num_kv_heads=8, seed=34)
+    g = H.gpu_setup(w)
+    H.gpu_step(w, g, attention=False)
+    o = H.oracle_run(w, attention=False)
+    table = np.asarray(g.plan.tables)
+    table[0, 20] = -1          # a block in the middle of the cached keys: its keys drop out
+    g.table = torch.tensor(table, dtype=torch.int32, device="cuda")
+    out, need = _splitk(w, g)
+    ref = OA.prefill_varlen(H.storage(w.q, "bf16"), o.k_pool, o.v_pool, g.plan.cu_q, g.plan.cu_k,
+                            table, w.scale, True, "bf16")
+    H.assert_close(H.out_f64(out), ref, "bf16", "split with an unassigned block")
+    small = torch.empty(need - 8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pa.PaError) as e:
+        _splitk(w, g, small, need)
+    assert e.value.code == -3
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_prefill_varlen_splitk(g.pool, out, g.q, g.cu_q, g.cu_k, g.plan.max_q, g.plan.max_k,
+                                    g.table, w.scale, True, None)
+    assert e.value.code == -3
+    out3, _ = _splitk(w, g, exact=True)
+    H.assert_close(H.out_f64(out3), ref, "bf16", "split from host lengths, unassigned block")
+
+
+# --------------------------------------------------------------------------------------
 # contiguous (non-paged) K/V
 # --------------------------------------------------------------------------------------
 
