@@ -89,15 +89,19 @@ __device__ __forceinline__ void pipeline_order() {
     }
 }
 
-template <int D, int G, int BS>  // BS = 0: contiguous K/V
+// BS = 0: contiguous K/V.  kSplit: jobs may be cut into key ranges (n_split, split_tiles);
+// without it those arguments are ignored and the kernel is the plain one.
+template <int D, int G, int BS, bool kSplit>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, const int32_t* __restrict__ block_table,
     uint16_t* __restrict__ out, int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks,
     int32_t max_blocks, float qscale, int32_t causal, int32_t n_qtiles, int32_t n_groups,
-    int32_t n_split, int32_t split_tiles, float* __restrict__ part_o,
+    int32_t n_split_arg, int32_t split_tiles_arg, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
+    const int n_split = kSplit ? n_split_arg : 1;
+    const int split_tiles = kSplit ? split_tiles_arg : 0;
     constexpr int BN = kPrefillKeys;
     constexpr bool kPaged = BS > 0;
     constexpr int PBS = kPaged ? BS : BN;        // keys per page (one page per tile when contiguous)
@@ -568,7 +572,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 
     // normalise and store: lane holds d = 32db + 8i + 4h + jj of its row
     const float lt = l + __shfl_xor(l, 32);
-    if (n_split_job > 1) {
+    if (kSplit && n_split_job > 1) {
         // one key range of a split job: the unnormalised O, the reference max m and l
         // of each row go to the workspace, for prefill_merge_kernel
         if (!row_ok) return;
@@ -795,13 +799,22 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
     float2* part_ml = sp.n_split > 1
         ? reinterpret_cast<float2*>(part_o + static_cast<size_t>(sp.units) * kPrefillRows * D) : nullptr;
     const dim3 grid(static_cast<uint32_t>(padded));
-    hipLaunchKernelGGL((prefill_kernel<D, G, BS>), grid, dim3(kPrefillThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const char*>(kv.k),
-                       static_cast<const char*>(kv.v), cu_q, cu_k, kv.table,
-                       static_cast<uint16_t*>(out), num_heads, kv.num_kv_heads,
-                       kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
-                       static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups),
-                       sp.n_split, sp.split_tiles, part_o, part_ml);
+    if (sp.n_split > 1)
+        hipLaunchKernelGGL((prefill_kernel<D, G, BS, true>), grid, dim3(kPrefillThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const char*>(kv.k),
+                           static_cast<const char*>(kv.v), cu_q, cu_k, kv.table,
+                           static_cast<uint16_t*>(out), num_heads, kv.num_kv_heads,
+                           kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
+                           static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups),
+                           sp.n_split, sp.split_tiles, part_o, part_ml);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, G, BS, false>), grid, dim3(kPrefillThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const char*>(kv.k),
+                           static_cast<const char*>(kv.v), cu_q, cu_k, kv.table,
+                           static_cast<uint16_t*>(out), num_heads, kv.num_kv_heads,
+                           kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
+                           static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups), 1, 0,
+                           nullptr, nullptr);
     if (sp.n_split > 1) {
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
         const int64_t chunks = kPrefillRows / (kMergeThreads / (D / 4));  // workgroups per job
