@@ -32,14 +32,20 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 
 WORKLOADS = ("qwen3_decode_b64", "long_decode_b8", "shared_prefix_decode_b128",
-             "chunked_prefill_r16")
+             "chunked_prefill_r16", "prompt_chunk_7680_512")
+# prefill workloads timed through pa_prefill_varlen_splitk (key splitting) rather than
+# pa_prefill_varlen: one 512-token chunk of a long prompt after 7680 cached tokens, a batch
+# with far fewer jobs than the GPU has workgroup slots
+SPLIT_WORKLOADS = ("prompt_chunk_7680_512",)
 
 
 def make_workload(name: str, seed: int):
     from paged_kv_cache_73_amd import workloads as W
     return {"qwen3_decode_b64": W.qwen3_decode, "long_decode_b8": W.long_decode,
             "shared_prefix_decode_b128": W.shared_prefix_decode,
-            "chunked_prefill_r16": W.chunked_prefill}[name](seed=seed)
+            "chunked_prefill_r16": W.chunked_prefill,
+            "prompt_chunk_7680_512": lambda seed: W.prefill_workload(
+                [7680], [512], seed=seed, name="prompt_chunk_7680_512")}[name](seed=seed)
 
 
 def decode_bytes(w, plan) -> int:
@@ -174,10 +180,18 @@ def main() -> int:
         R.ensure_workspace(w, r, P)
     torch.cuda.synchronize()
 
+    split = w.name in SPLIT_WORKLOADS
+
+    def attend():
+        if split:
+            R.attend_splitk(w, r)
+        else:
+            R.attend(w, r, P)
+
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         R.write(w, r)
-        R.attend(w, r, P)
+        attend()
     torch.cuda.synchronize()
 
     # Events on the kernels' stream: decode brackets its first pass (the kernel that reads
@@ -193,7 +207,7 @@ def main() -> int:
             mid.record(stream)
             R.attend_merge(w, r, P)
         else:
-            R.attend(w, r, P)
+            attend()
             mid.record(stream)
         b.record(stream)
     torch.cuda.synchronize()
@@ -217,7 +231,7 @@ def main() -> int:
             b.record(stream)
             R.attend_merge(w, r, P)
         else:
-            R.attend(w, r, P)
+            attend()
             b.record(stream)
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b))
@@ -284,6 +298,23 @@ def main() -> int:
                       "launch_us_median": 1e3 * cms[len(cms) // 2]}
         del kc, vc
 
+    # a split workload: the same prefill through the unsplit call, for comparison
+    unsplit = None
+    if split:
+        for _ in range(args.warmup):
+            R.attend(w, r, P)
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in pev:
+            a.record(stream)
+            R.attend(w, r, P)
+            b.record(stream)
+        torch.cuda.synchronize()
+        pms = sorted(a.elapsed_time(b) for a, b in pev)
+        unsplit = {"call": "pa_prefill_varlen", "launch_us_mean": 1e3 * sum(pms) / len(pms),
+                   "launch_us_median": 1e3 * pms[len(pms) // 2]}
+
     plan = r.plan
     csrc = os.path.join(ROOT, "paged_kv_cache_73_amd", "csrc")
     kernel_src = ([os.path.join(csrc, "decode_kernel.h"), os.path.join(csrc, "decode.hip")]
@@ -329,13 +360,18 @@ def main() -> int:
                 "value": fl / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s"}
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
-                "traffic": load_traffic(kernel_src, w.name), "kernel": "pa_prefill_varlen",
+                "traffic": load_traffic(kernel_src, w.name),
+                "kernel": ("pa_prefill_varlen_splitk (prefill_kernel key ranges + prefill_merge_kernel)"
+                           if split else "pa_prefill_varlen"),
                 "algorithmic_flops_per_launch": fl, "launch_us_mean": attn_mean_ms * 1e3,
                 "launch_us_median": attn_median_ms * 1e3,
                 "cold_launch_us_median": None if cold_median_ms is None else cold_median_ms * 1e3,
                 "contiguous_kv": contiguous}
         if contiguous:
             contiguous["achieved"] = fl / (contiguous["launch_us_mean"] * 1e-6) / 1e12
+        if unsplit:
+            unsplit["achieved"] = fl / (unsplit["launch_us_mean"] * 1e-6) / 1e12
+            roof["unsplit"] = unsplit
     line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                  "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
                  "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",

@@ -36,6 +36,7 @@ class DeviceRun:
     copy_src: torch.Tensor
     copy_dst: torch.Tensor
     workspace: torch.Tensor | None = None
+    prefill_ws: torch.Tensor | None = None
 
 
 def _i32(x, dev) -> torch.Tensor:
@@ -86,6 +87,20 @@ def attend(w: W.Workload, r: DeviceRun, partition_tokens: int = 0) -> None:
     else:
         pa.pa_prefill_varlen(r.pool, r.out, r.q, r.cu_q, r.cu_k, r.plan.max_q, r.plan.max_k,
                              r.table, w.scale, w.causal)
+
+
+def attend_splitk(w: W.Workload, r: DeviceRun) -> None:
+    """The prefill with key splitting (pa_prefill_varlen_splitk), planned from host copies
+    of the lengths; the workspace is sized once per run."""
+    hq, hk = r.plan.cu_q, r.plan.cu_k
+    if r.prefill_ws is None:
+        dt = pa.PA_BF16 if w.dtype == "bf16" else pa.PA_F32
+        need = pa.pa_prefill_workspace_bytes(dt, w.batch, w.num_heads, w.num_kv_heads,
+                                             w.head_dim, w.block_size, r.plan.max_q,
+                                             r.plan.max_k, w.causal, hq, hk)
+        r.prefill_ws = torch.empty(max(need, 1), dtype=torch.uint8, device=r.q.device)
+    pa.pa_prefill_varlen_splitk(r.pool, r.out, r.q, r.cu_q, r.cu_k, r.plan.max_q, r.plan.max_k,
+                                r.table, w.scale, w.causal, r.prefill_ws, hq, hk)
 
 
 def attend_contiguous(w: W.Workload, r: DeviceRun, k: torch.Tensor, v: torch.Tensor) -> None:
