@@ -127,9 +127,15 @@ int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src, const int32_t* ds
  *   Keys are cut into partitions processed by different workgroups; each yields an
  *   online-softmax state (m, l, o) and a second kernel merges them with the [PA11]
  *   §11.2 rule.  Sequences with one partition are finished by the first kernel.
+ * Large groups: bf16 pools with head_dim 64 or 128, B 16 or 32 and 5-8, 16 or 32 query
+ *   heads per KV head run on the matrix-core kernel of pa_prefill_varlen (one query
+ *   row per head, the group's heads sharing each key tile), with sequence offsets built
+ *   from seqlens_k on the device; partition_tokens is then rounded up to whole 64-key
+ *   tiles, and 0 takes the key-split plan of pa_prefill_varlen_splitk.  Such shapes
+ *   always need a workspace.
  * workspace: device scratch of at least pa_decode_workspace_bytes(...) bytes, called with
  *   the same batch, heads, head_dim, max_seqlen_k, partition_tokens and block size (may
- *   be NULL when that is 0).  Its contents need no initialisation and are meaningless
+ *   be NULL when that is 0; it covers either route, as the dtype is not an argument).  Its contents need no initialisation and are meaningless
  *   after the call; calls that share a workspace must not overlap.
  * Errors: PA_ERR_INVALID_ARG (null pointers, num_heads not a multiple of num_kv_heads,
  *   partition_tokens not a multiple of B), PA_ERR_WORKSPACE, PA_ERR_UNSUPPORTED (shape,
@@ -177,7 +183,8 @@ int pa_decode_merge(const pa_kv_pool* pool, void* out, int32_t batch, int32_t nu
  * attended.  The position's block must be private and assigned (pa_bm_prepare_write,
  * then pa_copy_blocks for its copy-on-write pairs); if its id is outside the pool the
  * row is neither stored nor attended.  Equivalent to pa_write_kv with those slots
- * followed by pa_decode, in one launch fewer.
+ * followed by pa_decode, bit for bit (on the vector-unit kernel in one launch fewer; on
+ * the large-group route the store is a small kernel of its own).
  * ------------------------------------------------------------------------------- */
 int pa_decode_append(const pa_kv_pool* pool, void* out, const void* q, const void* k_new,
                      const void* v_new, int32_t batch, int32_t num_heads,

@@ -93,6 +93,10 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// The two passes of a split-K attention call: partial states (and the rows finished in
+// one piece), then their merge.
+constexpr int kPass1 = 1, kPass2 = 2;
+
 inline int launch_status() {
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

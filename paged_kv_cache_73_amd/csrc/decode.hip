@@ -95,6 +95,18 @@ int dispatch_shape(int G, const pa_kv_pool* pool, void* out, const void* q, int3
     return PA_ERR_UNSUPPORTED;
 }
 
+// large GQA groups in bf16 run on the matrix-core kernel of prefill.hip
+bool decode_mc_shape(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size);
+bool decode_on_matrix_cores(const pa_kv_pool* pool, int32_t num_heads);
+size_t decode_mc_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seqlen_k, int32_t partition_tokens);
+int decode_mc(const pa_kv_pool* pool, void* out, const void* q, const void* k_new,
+              const void* v_new, int32_t batch, int32_t num_heads, const int32_t* table,
+              int32_t max_blocks, const int32_t* seqlens, int32_t max_seqlen_k, float scale,
+              int32_t partition_tokens, void* workspace, size_t workspace_size, hipStream_t s,
+              int passes);
+
 inline size_t workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
                               int32_t max_parts) {
     if (max_parts <= 1) return 0;
@@ -116,7 +128,11 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads,
         return 0;
     const int32_t p = pick_partition(partition_tokens, block_size, head_dim, batch, num_kv_heads,
                                      max_seqlen_k);
-    return workspace_bytes(batch, num_heads, head_dim, num_parts(max_seqlen_k, p));
+    const size_t valu = workspace_bytes(batch, num_heads, head_dim, num_parts(max_seqlen_k, p));
+    // the dtype is not known here: enough for either route
+    if (!decode_mc_shape(num_heads, num_kv_heads, head_dim, block_size)) return valu;
+    return std::max(valu, decode_mc_workspace_bytes(batch, num_heads, num_kv_heads, head_dim,
+                                                    max_seqlen_k, partition_tokens));
 }
 
 namespace pa {
@@ -143,6 +159,11 @@ int decode_impl(const pa_kv_pool* pool, void* out, const void* q, const void* k_
         const int32_t bs = pool->block_size;
         if (bs != 2 && bs != 4 && bs != 8 && bs != 16 && bs != 32) return PA_ERR_UNSUPPORTED;
     }
+    if (decode_on_matrix_cores(pool, num_heads))
+        return decode_mc(pool, out, q, k_new, v_new, batch, num_heads, block_table,
+                         max_blocks_per_seq, seqlens_k, max_seqlen_k, softmax_scale,
+                         partition_tokens, workspace, workspace_size,
+                         static_cast<hipStream_t>(stream), passes);
     const int32_t part_tokens = pick_partition(partition_tokens, pool->block_size, pool->head_dim,
                                                batch, pool->num_kv_heads, max_seqlen_k);
     if (part_tokens % pool->block_size != 0) return PA_ERR_INVALID_ARG;

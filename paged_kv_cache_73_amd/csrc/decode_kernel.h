@@ -91,10 +91,6 @@ __device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[E], int
     m = m_new;
 }
 
-// The two passes of a split-K decode: partial states (and the rows of single-partition
-// sequences), then their merge.
-constexpr int kPass1 = 1, kPass2 = 2;
-
 // Packed query tokens in place of sequences (the varlen prefill run token by token):
 // "sequence" b is query token offset + blockIdx.z of the packed batch, its request is
 // the one whose [cu_q[i], cu_q[i+1]) holds it, and it attends to that request's first

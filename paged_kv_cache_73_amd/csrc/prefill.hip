@@ -271,7 +271,10 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int wave_first = min(tok0 + (w * 32) / G, q_len - 1);
     const int wave_last = min(tok0 + (kAllRows ? w * 32 + 31 : min(w * 32 + 31, TOK * G - 1)) / G, q_len - 1);
     const int wave_lo = min(causal ? cached + wave_first : k_len - 1, kv_end - 1);  // all rows see keys <= this
-    const int wave_hi = min(causal ? cached + wave_last : k_len - 1, kv_end - 1);   // no row sees keys > this
+    // no row sees keys > this; -1 for a wave whose rows all lie past the request's queries
+    // (the last query tile of a request, a one-token request): it only stages K/V
+    const bool wave_rows = tok0 + (w * 32) / G < q_len;
+    const int wave_hi = wave_rows ? min(causal ? cached + wave_last : k_len - 1, kv_end - 1) : -1;
 
     // q row of this lane, pieces 16s + 8h .. +8 of the head dim
     bf16x8_t qf[KS];
@@ -789,7 +792,7 @@ template <int D, int G, int BS>
 int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                    int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
                    int32_t max_seqlen_q, float scale, int32_t causal, hipStream_t stream,
-                   const SplitPlan& sp, void* workspace) {
+                   const SplitPlan& sp, void* workspace, int passes) {
     const int tok_per_wg = kPrefillRows / G;
     const int64_t n_qtiles = (max_seqlen_q + tok_per_wg - 1) / tok_per_wg;
     const int64_t n_groups = static_cast<int64_t>(kv.num_kv_heads) * batch;
@@ -799,7 +802,9 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
     float2* part_ml = sp.n_split > 1
         ? reinterpret_cast<float2*>(part_o + static_cast<size_t>(sp.units) * kPrefillRows * D) : nullptr;
     const dim3 grid(static_cast<uint32_t>(padded));
-    if (sp.n_split > 1)
+    if (!(passes & kPass1)) {
+        // the merge alone (of ranges stored by an earlier call)
+    } else if (sp.n_split > 1)
         hipLaunchKernelGGL((prefill_kernel<D, G, BS, true>), grid, dim3(kPrefillThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const char*>(kv.k),
                            static_cast<const char*>(kv.v), cu_q, cu_k, kv.table,
@@ -815,7 +820,7 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                            kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
                            static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups), 1, 0,
                            nullptr, nullptr);
-    if (sp.n_split > 1) {
+    if (sp.n_split > 1 && (passes & kPass2)) {
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
         const int64_t chunks = kPrefillRows / (kMergeThreads / (D / 4));  // workgroups per job
         hipLaunchKernelGGL((prefill_merge_kernel<D, G, BS>), dim3(static_cast<uint32_t>(n_groups * n_qtiles * chunks)),
@@ -831,9 +836,9 @@ template <int D>
 int dispatch_prefill_group(int G, const KvSource& kv, void* out, const void* q, int32_t batch,
                            int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
                            int32_t max_seqlen_q, float scale, int32_t causal,
-                           hipStream_t stream, const SplitPlan& sp, void* workspace) {
+                           hipStream_t stream, const SplitPlan& sp, void* workspace, int passes) {
 #define PA_PREFILL_LAUNCH(GG, BB) \
-    launch_prefill<D, GG, BB>(kv, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, scale, causal, stream, sp, workspace)
+    launch_prefill<D, GG, BB>(kv, out, q, batch, num_heads, cu_q, cu_k, max_seqlen_q, scale, causal, stream, sp, workspace, passes)
 #define PA_PREFILL_CASE(GG)                                                                     \
     case GG:                                                                                    \
         if (!kv.paged) return PA_PREFILL_LAUNCH(GG, 0);                              \
@@ -858,17 +863,172 @@ int dispatch_prefill_group(int G, const KvSource& kv, void* out, const void* q, 
 int prefill_impl(const KvSource& kv, int32_t head_dim, void* out, const void* q, int32_t batch,
                  int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
                  int32_t max_seqlen_q, float scale, int32_t causal, hipStream_t s,
-                 const SplitPlan& sp = SplitPlan{1, 0, 0}, void* workspace = nullptr) {
+                 const SplitPlan& sp = SplitPlan{1, 0, 0}, void* workspace = nullptr,
+                 int passes = kPass1 | kPass2) {
     if (num_heads % kv.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
     if (!(scale > 0.f) || scale == INFINITY) return PA_ERR_INVALID_ARG;
     const int G = num_heads / kv.num_kv_heads;
     if (head_dim == 128)
         return dispatch_prefill_group<128>(G, kv, out, q, batch, num_heads, cu_q, cu_k,
-                                           max_seqlen_q, scale, causal != 0, s, sp, workspace);
+                                           max_seqlen_q, scale, causal != 0, s, sp, workspace,
+                                           passes);
     if (head_dim == 64)
         return dispatch_prefill_group<64>(G, kv, out, q, batch, num_heads, cu_q, cu_k,
-                                          max_seqlen_q, scale, causal != 0, s, sp, workspace);
+                                          max_seqlen_q, scale, causal != 0, s, sp, workspace,
+                                          passes);
     return PA_ERR_UNSUPPORTED;
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode with large GQA groups on the matrix cores.  The decode kernel (decode_kernel.h)
+// computes each lane's dot products on the vector unit, G query heads at a time; from
+// five query heads per KV head on, that vector work, not HBM, sets its pace (64 query /
+// 8 KV heads: 2.4 TB/s).  A decode step is also a varlen prefill with one query token
+// per sequence: the G heads of a KV head are G rows of one job of this file's kernel,
+// whose products run on the matrix cores, with a key-split plan in place of the decode
+// partitions.  pa_decode, its two passes and pa_decode_append take this route for such
+// shapes; the workspace holds cu_seqlens built from seqlens, then the split states.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kDecodeMcMinGroup = 5;
+
+// the shapes (dtype aside: bf16 only) that take this route
+bool decode_mc_shape(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size) {
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return false;
+    const int G = num_heads / num_kv_heads;
+    const bool group = (G >= kDecodeMcMinGroup && G <= 8) || G == 16 || G == 32;
+    return group && (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
+}
+
+bool decode_on_matrix_cores(const pa_kv_pool* pool, int32_t num_heads) {
+    return pool->dtype == PA_BF16 &&
+           decode_mc_shape(num_heads, pool->num_kv_heads, pool->head_dim, pool->block_size);
+}
+
+inline size_t decode_mc_header(int32_t batch) {
+    return (2 * (static_cast<size_t>(batch) + 1) * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+// Key ranges: of partition_tokens keys (rounded up to whole 64-key tiles) when given.
+// Else ranges long enough for about kDecodeTargetUnits (job, range) units over the
+// longest sequence, of at least kDecodeMinSplitTiles tiles, and of up to kDecodeSplitTiles
+// while that still leaves kDecodeFewUnits units: a decode job has one query row per head,
+// so a range's fixed costs weigh more than in a prefill.  (Measured on 64 query / 8 or 4
+// KV heads: 4 sequences of 16K keys and 16 of 8K ran fastest in ranges of 16 tiles, 64
+// sequences of 4K in two ranges rather than four, 8 of 40K in 16 ranges of 40 tiles.)
+constexpr int64_t kDecodeTargetUnits = 1024;
+constexpr int64_t kDecodeFewUnits = 512;
+constexpr int64_t kDecodeMinSplitTiles = 16;
+constexpr int64_t kDecodeSplitTiles = 32;
+
+inline SplitPlan decode_mc_plan(int32_t batch, int32_t num_kv_heads, int32_t max_seqlen_k,
+                                int32_t partition_tokens) {
+    SplitPlan p{1, 0, 0};
+    const int64_t longest = (static_cast<int64_t>(max_seqlen_k) + kPrefillKeys - 1) / kPrefillKeys;
+    const int64_t work = longest * batch * num_kv_heads;  // tiles of the longest jobs
+    const int64_t st = partition_tokens > 0
+        ? (static_cast<int64_t>(partition_tokens) + kPrefillKeys - 1) / kPrefillKeys
+        : std::max({kDecodeMinSplitTiles, (work + kDecodeTargetUnits - 1) / kDecodeTargetUnits,
+                    std::min(kDecodeSplitTiles, work / kDecodeFewUnits)});
+    if (longest <= st) return p;
+    p.n_split = static_cast<int32_t>((longest + st - 1) / st);
+    p.split_tiles = static_cast<int32_t>(st);
+    p.units = static_cast<int64_t>(batch) * num_kv_heads * p.n_split;
+    return p;
+}
+
+size_t decode_mc_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seqlen_k, int32_t partition_tokens) {
+    return decode_mc_header(batch) +
+           split_workspace_bytes(decode_mc_plan(batch, num_kv_heads, max_seqlen_k, partition_tokens),
+                                 head_dim);
+}
+
+// cu_q[i] = i; cu_k = running sum of max(seqlens, 0), kept modulo 2^32 (only
+// differences of consecutive entries are read).  One workgroup.
+__global__ __launch_bounds__(1024) void decode_cu_kernel(const int32_t* __restrict__ seqlens,
+                                                          int32_t batch, int32_t* __restrict__ cu_q,
+                                                          int32_t* __restrict__ cu_k) {
+    __shared__ uint32_t part[1024];
+    const int t = threadIdx.x;
+    const int per = (batch + 1023) / 1024;
+    const int lo = min(t * per, batch), hi = min(lo + per, batch);
+    uint32_t sum = 0;
+    for (int i = lo; i < hi; ++i) sum += static_cast<uint32_t>(max(seqlens[i], 0));
+    part[t] = sum;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the thread sums
+        const uint32_t v = t >= off ? part[t - off] : 0u;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    uint32_t run = t > 0 ? part[t - 1] : 0u;
+    for (int i = lo; i < hi; ++i) {
+        cu_k[i] = static_cast<int32_t>(run);
+        cu_q[i] = i;
+        run += static_cast<uint32_t>(max(seqlens[i], 0));
+    }
+    if (t == 1023) {
+        cu_k[batch] = static_cast<int32_t>(part[1023]);
+        cu_q[batch] = batch;
+    }
+}
+
+// pa_decode_append's write on this route: the new K/V row of sequence b goes to position
+// seqlens[b] - 1 through its table row (skipped when that block is unassigned), as the
+// decode kernel's fused append stores it.  One workgroup per sequence.
+__global__ __launch_bounds__(kWave) void decode_append_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    const int32_t* __restrict__ seqlens, const int32_t* __restrict__ table, int32_t max_blocks,
+    int32_t block_size, int32_t num_blocks, int32_t row_vecs, uint4* __restrict__ k_cache,
+    uint4* __restrict__ v_cache) {
+    const int b = blockIdx.x;
+    const int64_t cap = static_cast<int64_t>(max_blocks) * block_size;
+    const int64_t len = min(static_cast<int64_t>(max(seqlens[b], 0)), cap);
+    if (len <= 0) return;
+    const int64_t pos = len - 1;
+    const int32_t id = table[static_cast<int64_t>(b) * max_blocks + pos / block_size];
+    if (id < 0 || id >= num_blocks) return;
+    const int64_t slot = static_cast<int64_t>(id) * block_size + pos % block_size;
+    for (int i = threadIdx.x; i < row_vecs; i += kWave) {
+        k_cache[slot * row_vecs + i] = k_new[static_cast<int64_t>(b) * row_vecs + i];
+        v_cache[slot * row_vecs + i] = v_new[static_cast<int64_t>(b) * row_vecs + i];
+    }
+}
+
+int decode_mc(const pa_kv_pool* pool, void* out, const void* q, const void* k_new,
+              const void* v_new, int32_t batch, int32_t num_heads, const int32_t* table,
+              int32_t max_blocks, const int32_t* seqlens, int32_t max_seqlen_k, float scale,
+              int32_t partition_tokens, void* workspace, size_t workspace_size, hipStream_t s,
+              int passes) {
+    const SplitPlan sp = decode_mc_plan(batch, pool->num_kv_heads, max_seqlen_k, partition_tokens);
+    const size_t need = decode_mc_header(batch) + split_workspace_bytes(sp, pool->head_dim);
+    if (workspace == nullptr || workspace_size < need) return PA_ERR_WORKSPACE;
+    int32_t* cu_q = static_cast<int32_t*>(workspace);
+    int32_t* cu_k = cu_q + batch + 1;
+    void* states = static_cast<char*>(workspace) + decode_mc_header(batch);
+    if (passes & kPass1) {
+        hipLaunchKernelGGL(decode_cu_kernel, dim3(1), dim3(1024), 0, s, seqlens, batch, cu_q, cu_k);
+        if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+        if (k_new != nullptr) {
+            const int32_t row_vecs = pool->num_kv_heads * pool->head_dim * 2 / 16;
+            hipLaunchKernelGGL(decode_append_kernel, dim3(batch), dim3(kWave), 0, s,
+                               static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                               seqlens, table, max_blocks, pool->block_size, pool->num_blocks,
+                               row_vecs, static_cast<uint4*>(pool->k_cache),
+                               static_cast<uint4*>(pool->v_cache));
+            if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+        }
+    } else if (sp.n_split <= 1) {
+        return PA_OK;  // the first pass finished every row
+    }
+    const KvSource kv{true, pool->k_cache, pool->v_cache, pool->num_kv_heads, pool->num_blocks,
+                      pool->block_size, table, max_blocks};
+    // one query token per sequence, all its keys visible (non-causal is the same here)
+    return prefill_impl(kv, pool->head_dim, out, q, batch, num_heads, cu_q, cu_k, 1,
+                        scale, 0, s, sp, states, passes);
 }
 
 }  // namespace pa

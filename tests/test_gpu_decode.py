@@ -158,6 +158,10 @@ SHAPES = [  # (dtype, Hq, Hkv, d, B)
     ("bf16", 32, 2, 128, 16),
     ("f32", 16, 1, 64, 32),
     ("bf16", 32, 1, 128, 8),
+    # five or more query heads per KV head in bf16 at d 64/128, B 16/32: the matrix-core route
+    ("bf16", 64, 8, 128, 16),
+    ("bf16", 12, 2, 64, 16),
+    ("bf16", 64, 2, 128, 32),
 ]
 
 
@@ -231,8 +235,9 @@ def test_decode_edge_cases():
     assert not g.out.float().abs().sum().item()
 
 
-def test_decode_unassigned_block_is_masked():
-    w = W.decode_workload([40, 40], dtype="f32", num_heads=4, num_kv_heads=2, head_dim=64,
+@pytest.mark.parametrize("dtype,hq", [("f32", 4), ("bf16", 16)])
+def test_decode_unassigned_block_is_masked(dtype, hq):
+    w = W.decode_workload([40, 40], dtype=dtype, num_heads=hq, num_kv_heads=2, head_dim=64,
                           block_size=16, seed=14)
     g = H.gpu_setup(w)
     H.gpu_step(w, g, attention=False)
@@ -242,15 +247,40 @@ def test_decode_unassigned_block_is_masked():
     table[1, 2] = 10 ** 6       # id beyond the pool: never read
     t = torch.tensor(table, dtype=torch.int32, device="cuda")
     pa.pa_decode(g.pool, g.out, g.q, t, g.seqlens, 41, w.scale, 16,
-                 torch.zeros(pa.pa_decode_workspace_bytes(2, 4, 2, 64, 41, 16, 16), dtype=torch.uint8,
-                             device="cuda"))
+                 torch.zeros(pa.pa_decode_workspace_bytes(2, hq, 2, 64, 41, 16, 16),
+                             dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     from oracle import attention as OA
     ref_table = table.copy()
     ref_table[1, 2] = -1        # the oracle's reading: an id outside the pool is unassigned
     ref = OA.decode(H.storage(w.q, w.dtype), o.k_pool, o.v_pool, ref_table, g.plan.seqlens_k,
                     w.scale, w.dtype)
-    H.assert_close(H.out_f64(g.out), ref, "f32", "masked blocks")
+    H.assert_close(H.out_f64(g.out), ref, dtype, "masked blocks")
+
+
+def test_decode_large_group_edge_cases():
+    # the matrix-core route (8 query heads per KV head): a single key gives its value
+    # exactly, zero keys give zeros, and a workspace one byte short is refused
+    w = W.decode_workload([0, 0, 0], dtype="bf16", num_heads=64, num_kv_heads=8, seed=19)
+    g, _ = _check_decode(w)
+    ref = w.v_new.repeat_interleave(8, dim=1)
+    assert torch.equal(g.out.cpu(), ref)
+    zero = torch.zeros_like(g.seqlens)
+    g.out.fill_(7)
+    # this route always takes a workspace (it holds the sequence offsets)
+    need = pa.pa_decode_workspace_bytes(3, 64, 8, 128, 0, 0, 16)
+    assert need > 0
+    pa.pa_decode(g.pool, g.out, g.q, g.table, zero, 0, w.scale, 0,
+                 torch.empty(need, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert not g.out.float().abs().sum().item()
+    need = pa.pa_decode_workspace_bytes(3, 64, 8, 128, 5000, 256, 16)
+    assert need > 0
+    small = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    lens = torch.full_like(g.seqlens, 1)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode(g.pool, g.out, g.q, g.table, lens, 5000, w.scale, 256, small)
+    assert e.value.code == -3
 
 
 def test_decode_workspace_and_argument_errors():
@@ -306,6 +336,8 @@ FUSED_CASES = [  # (cached lengths, dtype, Hq, Hkv, d, B, partition tokens)
     ([0, 1, 2, 9, 33], "bf16", 16, 8, 128, 2, 8),
     ([0, 1, 15, 16, 17, 300], "bf16", 28, 4, 128, 16, 0),
     ([0, 1, 15, 16, 17, 300], "bf16", 32, 2, 128, 16, 0),
+    ([0, 1, 15, 16, 17, 300, 1500], "bf16", 64, 8, 128, 16, 64),
+    ([0, 1, 31, 32, 33, 900], "bf16", 40, 8, 64, 32, 0),
 ]
 
 
@@ -381,9 +413,11 @@ def test_decode_append_edge_cases():
     assert e.value.code == -1
 
 
+@pytest.mark.parametrize("heads", [(16, 8), (64, 8)], ids=["G2", "G8"])
 @pytest.mark.parametrize("partition_tokens", [0, 64, 256])
-def test_decode_two_passes_equal_one_call(partition_tokens):
-    w = W.decode_workload([0, 1, 100, 700, 2047, 3000, 16], dtype="bf16", seed=23)
+def test_decode_two_passes_equal_one_call(partition_tokens, heads):
+    w = W.decode_workload([0, 1, 100, 700, 2047, 3000, 16], dtype="bf16", num_heads=heads[0],
+                          num_kv_heads=heads[1], seed=23)
     g = H.gpu_setup(w)
     H.gpu_step(w, g, partition_tokens)
     torch.cuda.synchronize()
