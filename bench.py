@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 
 WORKLOADS = ("qwen3_decode_b64", "long_decode_b8", "shared_prefix_decode_b128",
-             "chunked_prefill_r16", "prompt_chunk_7680_512")
+             "gqa8_decode_b64", "chunked_prefill_r16", "prompt_chunk_7680_512")
 # prefill workloads timed through pa_prefill_varlen_splitk (key splitting) rather than
 # pa_prefill_varlen: one 512-token chunk of a long prompt after 7680 cached tokens, a batch
 # with far fewer jobs than the GPU has workgroup slots
@@ -43,6 +43,7 @@ def make_workload(name: str, seed: int):
     from paged_kv_cache_73_amd import workloads as W
     return {"qwen3_decode_b64": W.qwen3_decode, "long_decode_b8": W.long_decode,
             "shared_prefix_decode_b128": W.shared_prefix_decode,
+            "gqa8_decode_b64": W.gqa8_decode,
             "chunked_prefill_r16": W.chunked_prefill,
             "prompt_chunk_7680_512": lambda seed: W.prefill_workload(
                 [7680], [512], seed=seed, name="prompt_chunk_7680_512")}[name](seed=seed)
@@ -317,8 +318,13 @@ def main() -> int:
 
     plan = r.plan
     csrc = os.path.join(ROOT, "paged_kv_cache_73_amd", "csrc")
+    # bf16 decode with 5-8, 16 or 32 query heads per KV head at head_dim 64/128 and block
+    # size 16/32 runs on the prefill kernel (the library's routing rule)
+    group = w.num_heads // w.num_kv_heads
+    on_mc = (w.kind == "decode" and w.dtype == "bf16" and w.head_dim in (64, 128)
+             and w.block_size in (16, 32) and (5 <= group <= 8 or group in (16, 32)))
     kernel_src = ([os.path.join(csrc, "decode_kernel.h"), os.path.join(csrc, "decode.hip")]
-                  if w.kind == "decode" else [os.path.join(csrc, "prefill.hip")])
+                  if w.kind == "decode" and not on_mc else [os.path.join(csrc, "prefill.hip")])
     cfg = {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
            "num_blocks": w.num_blocks, "seed": args.seed}
@@ -343,7 +349,9 @@ def main() -> int:
         call_mean_ms = sum(call_ms) / len(call_ms)
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kernel_src, w.name),
-                "kernel": "decode_partial_kernel (pa_decode_partials, pass 1 of pa_decode)",
+                "kernel": ("prefill_kernel key ranges (pa_decode_partials, pass 1 of pa_decode, "
+                           "matrix-core route)" if on_mc else
+                           "decode_partial_kernel (pa_decode_partials, pass 1 of pa_decode)"),
                 "algorithmic_bytes_per_launch": dbytes,
                 "launch_us_mean": attn_mean_ms * 1e3, "launch_us_median": attn_median_ms * 1e3,
                 "pa_decode_call_us_mean": call_mean_ms * 1e3,

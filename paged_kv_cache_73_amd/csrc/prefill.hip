@@ -620,15 +620,15 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     uint16_t* __restrict__ out, int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks,
     int32_t max_blocks, int32_t causal, int32_t n_qtiles, int32_t n_split, int32_t split_tiles,
-    const float* __restrict__ part_o, const float2* __restrict__ part_ml) {
+    int32_t chunks, const float* __restrict__ part_o, const float2* __restrict__ part_ml) {
     constexpr int BN = kPrefillKeys;
     constexpr bool kPaged = BS > 0;
     constexpr int TOK = kPrefillRows / G;
     constexpr int D4 = D / 4;
     constexpr int kMergeRows = kMergeThreads / D4;       // rows per workgroup
-    constexpr int kChunks = kPrefillRows / kMergeRows;  // workgroups per job
-    const int64_t job = blockIdx.x / kChunks;
-    const int row = (blockIdx.x % kChunks) * kMergeRows + threadIdx.x / D4;
+    // chunks: workgroups per job, enough for the rows of min(TOK, max_seqlen_q) tokens
+    const int64_t job = blockIdx.x / chunks;
+    const int row = (blockIdx.x % chunks) * kMergeRows + threadIdx.x / D4;
     const int d4 = threadIdx.x % D4;
     const int qtile = static_cast<int>(job % n_qtiles);
     const int hkv = static_cast<int>((job / n_qtiles) % num_kv_heads);
@@ -822,11 +822,16 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                            nullptr, nullptr);
     if (sp.n_split > 1 && (passes & kPass2)) {
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-        const int64_t chunks = kPrefillRows / (kMergeThreads / (D / 4));  // workgroups per job
+        // workgroups per job: the rows of the tokens a query tile can hold (one token per
+        // request in a decode step: G rows, not the tile's kPrefillRows)
+        const int64_t merge_rows = kMergeThreads / (D / 4);
+        const int64_t rows = static_cast<int64_t>(std::min(tok_per_wg, max_seqlen_q)) * G;
+        const int64_t chunks = (rows + merge_rows - 1) / merge_rows;
         hipLaunchKernelGGL((prefill_merge_kernel<D, G, BS>), dim3(static_cast<uint32_t>(n_groups * n_qtiles * chunks)),
                            dim3(kMergeThreads), 0, stream, cu_q, cu_k, static_cast<uint16_t*>(out),
                            num_heads, kv.num_kv_heads, kv.num_blocks, kv.max_blocks, causal,
                            static_cast<int32_t>(n_qtiles), sp.n_split, sp.split_tiles,
+                           static_cast<int32_t>(chunks),
                            static_cast<const float*>(part_o), static_cast<const float2*>(part_ml));
     }
     return launch_status();
@@ -946,32 +951,29 @@ size_t decode_mc_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_k
 }
 
 // cu_q[i] = i; cu_k = running sum of max(seqlens, 0), kept modulo 2^32 (only
-// differences of consecutive entries are read).  One workgroup.
-__global__ __launch_bounds__(1024) void decode_cu_kernel(const int32_t* __restrict__ seqlens,
+// differences of consecutive entries are read).  One wave: each lane sums a run of
+// sequences, a shuffle scan gives the lanes' offsets.
+__global__ __launch_bounds__(kWave) void decode_cu_kernel(const int32_t* __restrict__ seqlens,
                                                           int32_t batch, int32_t* __restrict__ cu_q,
                                                           int32_t* __restrict__ cu_k) {
-    __shared__ uint32_t part[1024];
     const int t = threadIdx.x;
-    const int per = (batch + 1023) / 1024;
+    const int per = (batch + kWave - 1) / kWave;
     const int lo = min(t * per, batch), hi = min(lo + per, batch);
     uint32_t sum = 0;
     for (int i = lo; i < hi; ++i) sum += static_cast<uint32_t>(max(seqlens[i], 0));
-    part[t] = sum;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the thread sums
-        const uint32_t v = t >= off ? part[t - off] : 0u;
-        __syncthreads();
-        part[t] += v;
-        __syncthreads();
+    uint32_t incl = sum;  // inclusive scan over the lanes
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off);
+        if (t >= off) incl += v;
     }
-    uint32_t run = t > 0 ? part[t - 1] : 0u;
+    uint32_t run = incl - sum;
     for (int i = lo; i < hi; ++i) {
         cu_k[i] = static_cast<int32_t>(run);
         cu_q[i] = i;
         run += static_cast<uint32_t>(max(seqlens[i], 0));
     }
-    if (t == 1023) {
-        cu_k[batch] = static_cast<int32_t>(part[1023]);
+    if (t == kWave - 1) {
+        cu_k[batch] = static_cast<int32_t>(incl);
         cu_q[batch] = batch;
     }
 }
@@ -1010,7 +1012,7 @@ int decode_mc(const pa_kv_pool* pool, void* out, const void* q, const void* k_ne
     int32_t* cu_k = cu_q + batch + 1;
     void* states = static_cast<char*>(workspace) + decode_mc_header(batch);
     if (passes & kPass1) {
-        hipLaunchKernelGGL(decode_cu_kernel, dim3(1), dim3(1024), 0, s, seqlens, batch, cu_q, cu_k);
+        hipLaunchKernelGGL(decode_cu_kernel, dim3(1), dim3(kWave), 0, s, seqlens, batch, cu_q, cu_k);
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
         if (k_new != nullptr) {
             const int32_t row_vecs = pool->num_kv_heads * pool->head_dim * 2 / 16;

@@ -169,6 +169,16 @@ def qwen3_decode(seed: int = 0, batch: int = 64, lo: int = 512, hi: int = 4096) 
     return decode_workload([c - 1 for c in ctx], seed=seed, name="qwen3_decode_b64")
 
 
+def gqa8_decode(seed: int = 0, batch: int = 64, lo: int = 512, hi: int = 4096) -> Workload:
+    """Decode with eight query heads per KV head (64 query / 8 KV heads, head_dim 128, the
+    attention shape of Llama-3-70B): batch 64, contexts uniform in [512, 4096], block
+    size 16.  In bf16 this group size runs on the matrix-core route."""
+    rng = random.Random(seed ^ 0x5EED)
+    ctx = [rng.randint(lo, hi) for _ in range(batch)]
+    return decode_workload([c - 1 for c in ctx], seed=seed, num_heads=64, num_kv_heads=8,
+                           head_dim=128, block_size=16, name="gqa8_decode_b64")
+
+
 def long_decode(seed: int = 0, batch: int = 8, lo: int = 32768, hi: int = 40960) -> Workload:
     """Long-context decode: batch 8, contexts uniform in [32768, 40960] (up to the 40K
     maximum length of Qwen3-0.6B); the split-K partition size is a call argument."""

@@ -456,6 +456,15 @@ def test_decode_qwen3_b64_full():
     _check_decode(w, 0)
 
 
+def test_decode_gqa8_b64_full():
+    # 64 query / 8 KV heads at batch 64 (the matrix-core route), automatic key split as
+    # timed; sampled sequences, among them the longest and the shortest
+    w = W.gqa8_decode(seed=0)
+    lens = [c + n for c, n in zip(w.cached, w.new)]
+    rows = sorted({0, 31, 63, lens.index(max(lens)), lens.index(min(lens))})
+    _check_decode(w, 0, rows=rows, what="gqa8 b64")
+
+
 @pytest.mark.parametrize("partition_tokens", [256, 512, 1024])
 def test_decode_long_context_split_k(partition_tokens):
     w = W.long_decode(seed=0)
