@@ -131,8 +131,9 @@ int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src, const int32_t* ds
  *   heads per KV head run on the matrix-core kernel of pa_prefill_varlen (one query
  *   row per head, the group's heads sharing each key tile), with sequence offsets built
  *   from seqlens_k on the device; partition_tokens is then rounded up to whole 64-key
- *   tiles, and 0 takes the key-split plan of pa_prefill_varlen_splitk.  Such shapes
- *   always need a workspace.
+ *   tiles, and 0 plans key ranges of 16-32 tiles (or the whole sequence).  Such shapes
+ *   always need a workspace, and softmax_scale must be positive and finite there
+ *   (PA_ERR_INVALID_ARG otherwise), as for pa_prefill_varlen.
  * workspace: device scratch of at least pa_decode_workspace_bytes(...) bytes, called with
  *   the same batch, heads, head_dim, max_seqlen_k, partition_tokens and block size (may
  *   be NULL when that is 0; it covers either route, as the dtype is not an argument).  Its contents need no initialisation and are meaningless
