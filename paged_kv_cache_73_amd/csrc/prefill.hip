@@ -1005,6 +1005,8 @@ int decode_mc(const pa_kv_pool* pool, void* out, const void* q, const void* k_ne
               int32_t max_blocks, const int32_t* seqlens, int32_t max_seqlen_k, float scale,
               int32_t partition_tokens, void* workspace, size_t workspace_size, hipStream_t s,
               int passes) {
+    // checked before any launch, so that a refused call leaves the pool untouched
+    if ((passes & kPass1) && (!(scale > 0.f) || scale == INFINITY)) return PA_ERR_INVALID_ARG;
     const SplitPlan sp = decode_mc_plan(batch, pool->num_kv_heads, max_seqlen_k, partition_tokens);
     const size_t need = decode_mc_header(batch) + split_workspace_bytes(sp, pool->head_dim);
     if (workspace == nullptr || workspace_size < need) return PA_ERR_WORKSPACE;

@@ -281,6 +281,27 @@ def test_decode_large_group_edge_cases():
     with pytest.raises(pa.PaError) as e:
         pa.pa_decode(g.pool, g.out, g.q, g.table, lens, 5000, w.scale, 256, small)
     assert e.value.code == -3
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for bad in (0.0, -0.5, float("inf")):  # the matrix-core route takes a positive scale
+        with pytest.raises(pa.PaError) as e:
+            pa.pa_decode(g.pool, g.out, g.q, g.table, lens, 1, bad, 0, ws)
+        assert e.value.code == -1
+
+
+def test_decode_large_group_two_passes_without_split():
+    # every sequence within one key range: the first pass finishes all rows and the
+    # merge call has nothing to do
+    w = W.decode_workload([0, 5, 300, 1000], dtype="bf16", num_heads=64, num_kv_heads=8, seed=24)
+    g, o = _check_decode(w, 0)
+    whole = g.out.clone()
+    g.out.fill_(7.0)
+    max_k = max(g.plan.seqlens_k)
+    pa.pa_decode_partials(g.pool, g.out, g.q, g.table, g.seqlens, max_k, w.scale, 0, g.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(g.out, whole)
+    pa.pa_decode_merge(g.pool, g.out, g.table, g.seqlens, max_k, 0, g.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(g.out, whole)
 
 
 def test_decode_workspace_and_argument_errors():
