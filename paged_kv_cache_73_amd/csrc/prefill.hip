@@ -920,11 +920,12 @@ inline size_t decode_mc_header(int32_t batch) {
 // longest sequence, of at least kDecodeMinSplitTiles tiles, and of up to kDecodeSplitTiles
 // while that still leaves kDecodeFewUnits units: a decode job has one query row per head,
 // so a range's fixed costs weigh more than in a prefill.  (Measured on 64 query / 8 or 4
-// KV heads: 4 sequences of 16K keys and 16 of 8K ran fastest in ranges of 16 tiles, 64
-// sequences of 4K in two ranges rather than four, 8 of 40K in 16 ranges of 40 tiles.)
+// KV heads: 4 sequences of 16K keys and 16 of 8K ran fastest in ranges of 12-16 tiles,
+// 64 sequences of 4K in two ranges rather than four, 8 of 40K in 16 ranges of 40 tiles;
+// 8 sequences of 4K with 40 / 8 heads in ranges of 8 tiles, 29 against 37 us at 16.)
 constexpr int64_t kDecodeTargetUnits = 1024;
 constexpr int64_t kDecodeFewUnits = 512;
-constexpr int64_t kDecodeMinSplitTiles = 16;
+constexpr int64_t kDecodeMinSplitTiles = 8;
 constexpr int64_t kDecodeSplitTiles = 32;
 
 inline SplitPlan decode_mc_plan(int32_t batch, int32_t num_kv_heads, int32_t max_seqlen_k,
