@@ -162,6 +162,10 @@ SHAPES = [  # (dtype, Hq, Hkv, d, B)
     ("bf16", 64, 8, 128, 16),
     ("bf16", 12, 2, 64, 16),
     ("bf16", 64, 2, 128, 32),
+    ("bf16", 32, 2, 64, 32),
+    ("bf16", 64, 2, 64, 16),
+    ("bf16", 64, 8, 128, 32),
+    ("bf16", 56, 8, 64, 16),
 ]
 
 
