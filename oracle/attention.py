@@ -8,6 +8,10 @@ Pins (tests/test_oracle_pins.py):
   * online_softmax_trace   -- printed trace of 题目2 and its closed form.
   * flash_tiles            -- printed m, l and correction factors of 题目3, plus the
                               closed-form dense result for the lost final O.
+  * copy_blocks            -- pools whose every element encodes its own position:
+                              destination blocks hold exactly the source blocks'
+                              codes in K and in V, every other block is untouched,
+                              an empty pair list is a no-op.
   * locate / element_offset-- 题目5 (table [3,1,5]) and the Sayfalı dikkat decode
                               example (cache_seqlens [30,32,70], B=32).
   * gather / decode        -- brute-force dense attention on the un-paged values,

@@ -220,6 +220,44 @@ def test_write_kv_bitwise_and_negative_slots():
     del rng
 
 
+def _coded_pool(tag, nb, B, hkv, d, dtype):
+    """A pool whose every element names itself: (tag, block, slot, head, dim) packed into
+    the storage word, so any block read from the wrong place, or not copied, shows.  In
+    float32 the codes are NaN payloads (quiet NaN, sign from the tag)."""
+    idx = np.arange(nb * B * hkv * d, dtype=np.uint32).reshape(nb, B, hkv, d)
+    if dtype == "bf16":
+        return ((idx & np.uint32(0x3FFF)) | np.uint32(tag << 14)).astype(np.uint16)
+    return (np.uint32(0x7FC00000 | (tag << 31)) | idx).view(np.float32)
+
+
+def check_copy_blocks():
+    """Copy-on-write data step ("Paged attention 与 online softmax" §11.3): before a shared
+    block is written, a new block receives its contents; the old block is left as it was.
+    Expected pools are built from the element codes directly (block s's codes moved to
+    block t), not by any copying routine."""
+    nb, B, hkv, d = 7, 2, 2, 4
+    for dtype in ("bf16", "f32"):
+        kp, vp = _coded_pool(0, nb, B, hkv, d, dtype), _coded_pool(1, nb, B, hkv, d, dtype)
+        k_before, v_before = kp.copy(), vp.copy()
+        pairs = [(4, 1), (0, 5), (6, 2)]
+        k2, v2 = A.copy_blocks(kp, vp, [s for s, _ in pairs], [t for _, t in pairs])
+        # the inputs are not modified
+        assert kp.tobytes() == k_before.tobytes() and vp.tobytes() == v_before.tobytes()
+        for tag, got in ((0, k2), (1, v2)):
+            want = _coded_pool(tag, nb, B, hkv, d, dtype)
+            for s, t in pairs:
+                want[t] = _coded_pool(tag, nb, B, hkv, d, dtype)[s]
+            assert got.dtype == want.dtype and got.shape == want.shape
+            assert got.tobytes() == want.tobytes(), f"{dtype} pool {tag}: copied blocks differ"
+        # an empty pair list changes nothing
+        k3, v3 = A.copy_blocks(kp, vp, [], [])
+        assert k3.tobytes() == kp.tobytes() and v3.tobytes() == vp.tobytes()
+
+
+def test_copy_blocks_bitwise():
+    check_copy_blocks()
+
+
 def test_bf16_codec():
     pats = np.array([0x3F80, 0xC000, 0x7F80, 0xFF80, 0x0001, 0x8000, 0x4049, 0x3EAA], dtype=np.uint16)
     got = A.bf16_bits_to_f64(pats)
@@ -670,6 +708,12 @@ def test_planted_mistakes_are_caught(monkeypatch, golden):
         m.setattr(A, "prefill_varlen_contiguous",
                   contiguous_variant(lambda cq, ck, i: ck[i], good_visible))
         check_contiguous_prefill()
+    # copy-on-write: (a) source and destination swapped, (b) only the K pool copied
+    orig_copy = A.copy_blocks
+    _caught(monkeypatch, A, "copy_blocks",
+            lambda k, v, src, dst: orig_copy(k, v, dst, src), check_copy_blocks)
+    _caught(monkeypatch, A, "copy_blocks",
+            lambda k, v, src, dst: (orig_copy(k, v, src, dst)[0], v.copy()), check_copy_blocks)
     # the freed block is appended at the bottom of the free stack
     # the prefix hash ignores the chaining
     with monkeypatch.context() as m:
