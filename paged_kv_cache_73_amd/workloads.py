@@ -170,9 +170,9 @@ def qwen3_decode(seed: int = 0, batch: int = 64, lo: int = 512, hi: int = 4096) 
 
 
 def gqa8_decode(seed: int = 0, batch: int = 64, lo: int = 512, hi: int = 4096) -> Workload:
-    """Decode with eight query heads per KV head (64 query / 8 KV heads, head_dim 128, the
-    attention shape of Llama-3-70B): batch 64, contexts uniform in [512, 4096], block
-    size 16.  In bf16 this group size runs on the matrix-core route."""
+    """Decode with eight query heads per KV head (64 query / 8 KV heads, head_dim 128):
+    batch 64, contexts uniform in [512, 4096], block size 16.  In bf16 this group size
+    runs on the matrix-core route."""
     rng = random.Random(seed ^ 0x5EED)
     ctx = [rng.randint(lo, hi) for _ in range(batch)]
     return decode_workload([c - 1 for c in ctx], seed=seed, num_heads=64, num_kv_heads=8,
