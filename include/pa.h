@@ -353,7 +353,8 @@ int pa_bm_allocate_prefix(pa_bm* bm, int32_t block_size, const int32_t* tokens,
 
 /* slots_out[i] = table[seq[i]][pos[i] / B] * B + pos[i] % B, or -1 when that entry is
  * unassigned ([QWEN] 自己来实现: slot_mapping is computed once and reused by every
- * layer).  table: [*][width]; PA_ERR_INVALID_ARG when pos[i]/B >= width or seq[i] < 0. */
+ * layer).  table: [*][width]; PA_ERR_INVALID_ARG when pos[i]/B >= width or seq[i] < 0,
+ * or when a slot would exceed INT32_MAX (slots are int32; nothing is written then). */
 int pa_build_slot_mapping(const int32_t* table, int32_t width, int32_t block_size,
                           const int32_t* seq, const int32_t* pos, int32_t n,
                           int32_t* slots_out);

@@ -296,12 +296,16 @@ int pa_build_slot_mapping(const int32_t* table, int32_t width, int32_t block_siz
     if (n < 0 || width < 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
     if (n > 0 && (table == nullptr || seq == nullptr || pos == nullptr || slots_out == nullptr))
         return PA_ERR_INVALID_ARG;
+    // slots are int32: a block whose slots lie past INT32_MAX cannot be named by one, and
+    // is refused (before any output is written) rather than wrapped
     for (int32_t i = 0; i < n; ++i) {
         if (seq[i] < 0 || pos[i] < 0 || pos[i] / block_size >= width) return PA_ERR_INVALID_ARG;
+        const int64_t phys = table[static_cast<int64_t>(seq[i]) * width + pos[i] / block_size];
+        if (phys >= 0 && phys * block_size + pos[i] % block_size > INT32_MAX) return PA_ERR_INVALID_ARG;
     }
     for (int32_t i = 0; i < n; ++i) {
-        const int32_t phys = table[static_cast<int64_t>(seq[i]) * width + pos[i] / block_size];
-        slots_out[i] = phys >= 0 ? phys * block_size + pos[i] % block_size : -1;
+        const int64_t phys = table[static_cast<int64_t>(seq[i]) * width + pos[i] / block_size];
+        slots_out[i] = phys >= 0 ? static_cast<int32_t>(phys * block_size + pos[i] % block_size) : -1;
     }
     return PA_OK;
 }

@@ -33,6 +33,7 @@
 //   the loader differs.
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 
@@ -728,18 +729,21 @@ struct SplitPlan {
     int64_t units;        // dense jobs x n_split: rows of the workspace
 };
 
-// workgroup slots of the current device: two per CU (the prefill kernel's occupancy)
+// workgroup slots of the current device: two per CU (the prefill kernel's occupancy).
+// The CU count is read once per device (each device of a process has its own entry).
 inline int64_t prefill_slots() {
-    static int64_t slots = 0;
-    if (slots == 0) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int32_t> cus_of[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int cus = dev < kMaxDevices ? cus_of[dev].load(std::memory_order_relaxed) : 0;
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        slots = 2 * static_cast<int64_t>(cus);
+        if (dev < kMaxDevices) cus_of[dev].store(cus, std::memory_order_relaxed);
     }
-    return slots;
+    return 2 * static_cast<int64_t>(cus);
 }
 
 inline SplitPlan plan_split(int32_t batch, int32_t num_heads, int32_t num_kv_heads,

@@ -156,6 +156,11 @@ def test_library_errors():
         pa.BlockManager(3, initial_order=[0, 0, 1])
     with pytest.raises(pa.PaError):
         pa.pa_build_slot_mapping([[0, 1]], 4, [0], [8])
+    # slots are int32: the last slot that fits is accepted, one past it is refused
+    top = (2**31 - 1) // 16
+    assert pa.pa_build_slot_mapping([[top]], 16, [0], [(2**31 - 1) % 16]).tolist() == [2**31 - 1]
+    with pytest.raises(pa.PaError):
+        pa.pa_build_slot_mapping([[top + 1, 0]], 16, [0, 0], [16, 0])
 
 
 def _random_ops(seed, manager, n_ops=400):
