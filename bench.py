@@ -59,6 +59,22 @@ def decode_bytes(w, plan) -> int:
     return keys * 2 * w.kv_dim * e + w.batch * 2 * w.num_heads * w.head_dim * e + pages * 4
 
 
+def decode_unique_bytes(w, plan) -> int:
+    """decode_bytes with every physical block counted once: a block that several tables
+    share (a shared prefix) is read from HBM once at best.  The rows of a block that count
+    are the most any of its sequences uses."""
+    e = w.elem_bytes
+    B = w.block_size
+    rows = {}
+    for row, n in zip(plan.tables, plan.seqlens_k):
+        for j in range(-(-n // B)):
+            blk = row[j]
+            rows[blk] = max(rows.get(blk, 0), min(B, n - j * B))
+    pages = sum(-(-n // B) for n in plan.seqlens_k)
+    return (sum(rows.values()) * 2 * w.kv_dim * e
+            + w.batch * 2 * w.num_heads * w.head_dim * e + pages * 4)
+
+
 def write_bytes(w, plan) -> int:
     """pa_write_kv reads each new K and V row and writes it once; copy-on-write
     copies read and write whole blocks of K and V."""
@@ -99,47 +115,131 @@ def load_traffic(kernel_files, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float, max_rows=None) -> dict:
-    """The CPU oracle (gather + two-pass softmax in float64), one thread, on the same
-    inputs, repeated for about ``seconds``."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
+
+# The oracle's inputs for the CPU baseline, set in the parent before its worker processes
+# are forked (they inherit them; nothing is pickled).  The GPU is not touched before then.
+_ORACLE = {}
+
+
+def _one_thread() -> None:
+    from threadpoolctl import threadpool_limits
+    _ORACLE["limit"] = threadpool_limits(limits=1)
+
+
+def _oracle_item(item) -> float:
+    """One unit of oracle work, and its algorithmic count: ("d", b) the decode of sequence
+    b (bytes); ("p", i, t0, t1) query rows t0..t1-1 of request i (flops).  Rows of a
+    request are computed as a request of their own whose keys end at the last row's causal
+    limit, which the oracle's pins show equal to the one-shot rows."""
     from oracle import attention as OA
+    o = _ORACLE
+    w = o["w"]
+    if item[0] == "d":
+        b = item[1]
+        OA.decode(o["q"][b:b + 1], o["k"], o["v"], o["table"][b:b + 1], [o["seqlens"][b]],
+                  w.scale, w.dtype)
+        return o["unit"][item]
+    _, i, t0, t1 = item
+    q_len, k_len = o["q_lens"][i], o["k_lens"][i]
+    ks = k_len - (q_len - t1) if w.causal else k_len
+    rows = slice(o["cu_q"][i] + t0, o["cu_q"][i] + t1)
+    OA.prefill_varlen(o["q"][rows], o["k"], o["v"], [0, t1 - t0], [0, ks], o["table"][i:i + 1],
+                      w.scale, w.causal, w.dtype)
+    return o["unit"][item]
+
+
+def cpu_baseline(w, seconds: float) -> dict:
+    """The CPU oracle (gather + two-pass softmax in float64) on the same inputs, timed on
+    one core and on all the host cores this process may use (a process pool, one BLAS
+    thread each, over sequences or over 64-row blocks of requests), each the median of
+    three runs of about ``seconds``.  Value: GB/s of the decode's algorithmic bytes, or
+    TFLOP/s of the prefill's algorithmic flops."""
+    import multiprocessing as mp
+    import statistics
+
+    import numpy as np
+
     from tests.harness import oracle_run, storage
 
     o = oracle_run(w, attention=False)
-    q = storage(w.q, w.dtype)
-    table = np.asarray(o.plan.tables)
-    with threadpool_limits(limits=1):
-        if w.kind == "decode":
-            rows = list(range(w.batch if max_rows is None else min(max_rows, w.batch)))
-            seq = [o.plan.seqlens_k[r] for r in rows]
-            reps, t0 = 0, time.perf_counter()
-            while True:
-                OA.decode(q[rows], o.k_pool, o.v_pool, table[rows], seq, w.scale, w.dtype)
-                reps += 1
-                el = time.perf_counter() - t0
-                if el >= seconds:
-                    break
-            keys = sum(seq) * reps
-            e = w.elem_bytes
-            nbytes = (keys * 2 * w.kv_dim * e + reps * len(rows) * 2 * w.num_heads * w.head_dim * e)
-            return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                    "seq_tokens_per_s": keys / el,
-                    "sample": f"{len(rows)} of {w.batch} sequences x {reps} passes "
-                              f"({el:.1f} s, float64 gather + two-pass softmax, 1 thread)"}
-        reps, t0 = 0, time.perf_counter()
+    plan = o.plan
+    e = w.elem_bytes
+    _ORACLE.update(w=w, q=storage(w.q, w.dtype), k=o.k_pool, v=o.v_pool,
+                   table=np.asarray(plan.tables), seqlens=plan.seqlens_k, cu_q=plan.cu_q,
+                   q_lens=list(w.new), k_lens=plan.seqlens_k, unit={})
+    unit = _ORACLE["unit"]
+    if w.kind == "decode":
+        items = [("d", b) for b in range(w.batch)]
+        for it in items:
+            unit[it] = plan.seqlens_k[it[1]] * 2 * w.kv_dim * e + 2 * w.num_heads * w.head_dim * e
+        per, scale, name = 1e9, "GB/s", "sequences"
+    else:
+        items = []
+        for i, (qn, c) in enumerate(zip(w.new, w.cached)):
+            for t0 in range(0, qn, 64):
+                t1 = min(qn, t0 + 64)
+                it = ("p", i, t0, t1)
+                items.append(it)
+                pairs = sum((c + t + 1) if w.causal else (c + qn) for t in range(t0, t1))
+                unit[it] = 4.0 * w.head_dim * w.num_heads * pairs
+        per, scale, name = 1e12, "TFLOP/s", "64-row blocks"
+    items.sort(key=lambda it: -unit[it])   # longest first: the pool balances better
+
+    # one core: items in order, cycling, until `seconds` have passed; median of 3 runs
+    _one_thread()
+    one = []
+    done_items = 0
+    for _ in range(3):
+        work, n, t0 = 0.0, 0, time.perf_counter()
         while True:
-            OA.prefill_varlen(q, o.k_pool, o.v_pool, o.plan.cu_q, o.plan.cu_k, table, w.scale,
-                              w.causal, w.dtype)
-            reps += 1
+            work += _oracle_item(items[n % len(items)])
+            n += 1
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
-        fl = prefill_flops(w, o.plan) * reps
-        return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-                "sample": f"all {w.batch} requests x {reps} passes ({el:.1f} s, 1 thread)"}
+        one.append(work / el / per)
+        done_items = n
+    rate1 = statistics.median(one)
+
+    # all cores: a forked pool (the parent has not touched the GPU), at most 16 workers
+    # (the host share of one GPU); each run covers the items enough times to last about
+    # `seconds` at the measured one-core rate times the worker count
+    nproc = os.cpu_count() or 1
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
+    workers = max(1, min(16, avail))
+    total = sum(unit[it] for it in items)
+    reps = max(1, round(seconds * workers * rate1 * per / total))
+    runs = []
+    with mp.get_context("fork").Pool(workers, initializer=_one_thread) as pool:
+        pool.map(_oracle_item, items[:workers], chunksize=1)   # workers up
+        for _ in range(3):
+            t0 = time.perf_counter()
+            work = sum(pool.imap_unordered(_oracle_item, items * reps, chunksize=1))
+            runs.append(work / (time.perf_counter() - t0) / per)
+    rate_all = statistics.median(runs)
+    _ORACLE.clear()
+    out = {"value": rate_all, "unit": scale, "cores": workers, "kind": "oracle",
+           "value_all_cores": rate_all, "cores_all": workers, "value_1core": rate1,
+           "runs_all_cores": runs, "runs_1core": one, "nproc": nproc, "cpus_allowed": avail,
+           "cpu_model": _cpu_model(),
+           "sample": (f"all {len(items)} {name} x {reps} per all-core run; one core: "
+                      f"{done_items} {name} per run (about {seconds:.0f} s); median of 3 runs "
+                      f"each; float64 gather + two-pass softmax, one BLAS thread per process")}
+    if w.kind == "decode":
+        keys = sum(plan.seqlens_k)
+        out["seq_tokens_per_s_all_cores"] = rate_all * per * keys / total
+    return out
 
 
 def main() -> int:
@@ -150,7 +250,8 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen3_decode_b64", choices=WORKLOADS)
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=2.5,
+                    help="length of each of the three one-core and all-core oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="decode launches timed after flushing the caches (reported apart)")
@@ -166,6 +267,10 @@ def main() -> int:
 
     import torch
 
+    w = make_workload(args.workload, args.seed)
+    # the CPU oracle first: its worker processes are forked before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+
     from paged_kv_cache_73_amd import _native
     if not os.path.exists(_native.LIB_PATH):
         from paged_kv_cache_73_amd import build as B
@@ -174,7 +279,6 @@ def main() -> int:
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    w = make_workload(args.workload, args.seed)
     r = R.setup(w, dev)
     P = args.partition_tokens
     if w.kind == "decode":
@@ -222,20 +326,22 @@ def main() -> int:
     # the same attention call after evicting L2 and the MALL by reading 1 GiB (a read
     # leaves clean lines, so the timed call pays no write-backs)
     flush = torch.ones(1 << 29, dtype=torch.float32, device=dev)
-    cold = []
+    cold, cold_call = [], []
     for _ in range(args.cold_reps):
         flush.sum()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, mid, b = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         a.record(stream)
         if w.kind == "decode":
             R.attend_partials(w, r, P)
-            b.record(stream)
+            mid.record(stream)
             R.attend_merge(w, r, P)
         else:
             attend()
-            b.record(stream)
+            mid.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        cold.append(a.elapsed_time(b))
+        cold.append(a.elapsed_time(mid))
+        cold_call.append(a.elapsed_time(b))
     # attainable read bandwidth: plain streaming read of 2 GiB (best of a few grids)
     import paged_kv_cache_73_amd as pa
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -258,6 +364,24 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     cold_median_ms = sorted(cold)[len(cold) // 2] if cold else None
+    cold_call_median_ms = sorted(cold_call)[len(cold_call) // 2] if cold_call else None
+
+    # copy-on-write copies of the step (pa_copy_blocks) timed on their own
+    cow = None
+    if r.copy_src.numel():
+        import paged_kv_cache_73_amd as pa
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in cev:
+            a.record(stream)
+            pa.pa_copy_blocks(r.pool, r.copy_src, r.copy_dst)
+            b.record(stream)
+        torch.cuda.synchronize()
+        cus = sorted(1e3 * a.elapsed_time(b) for a, b in cev)
+        cbytes = 4 * len(r.plan.copies) * w.block_size * w.kv_dim * w.elem_bytes
+        cow = {"pairs": len(r.plan.copies), "bytes": cbytes,
+               "us_mean": sum(cus) / len(cus), "us_median": cus[len(cus) // 2],
+               "achieved_GBps": cbytes / (sum(cus) / len(cus) * 1e-6) / 1e9}
 
     # the same step with the KV write fused into the decode launch (pa_decode_append)
     fused = None
@@ -330,7 +454,11 @@ def main() -> int:
            "num_blocks": w.num_blocks, "seed": args.seed}
     if w.kind == "decode":
         dbytes = decode_bytes(w, plan)
-        step_bytes = dbytes + write_bytes(w, plan)
+        # shared pages: the roofline numerator counts each physical block once (the
+        # logical count, every sequence's keys, is reported beside it)
+        ubytes = decode_unique_bytes(w, plan)
+        shared = ubytes != dbytes
+        step_bytes = ubytes + write_bytes(w, plan)
         keys = sum(plan.seqlens_k)
         achieved = dbytes / (attn_mean_ms * 1e-3) / 1e9
         cfg.update({"context_min": min(plan.seqlens_k), "context_max": max(plan.seqlens_k),
@@ -347,17 +475,37 @@ def main() -> int:
             "fused_append_step": fused,
         }
         call_mean_ms = sum(call_ms) / len(call_ms)
+        if shared:
+            achieved = ubytes / (attn_mean_ms * 1e-3) / 1e9
+            line["logical_bytes_per_launch"] = dbytes
+            line["logical_GBps_pass1"] = dbytes / (attn_mean_ms * 1e-3) / 1e9
+        rbytes = ubytes
+        line["headline"] = {
+            "what": ("whole pa_decode call (pass 1, merge and the gap between them), "
+                     "L2 and MALL evicted before each call"),
+            "us_median": None if cold_call_median_ms is None else cold_call_median_ms * 1e3,
+            "GBps": None if not cold_call_median_ms else rbytes / (cold_call_median_ms * 1e-3) / 1e9,
+            "frac_of_peak": None if not cold_call_median_ms else
+            rbytes / (cold_call_median_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "warm_us_mean": call_mean_ms * 1e3,
+            "warm_GBps": rbytes / (call_mean_ms * 1e-3) / 1e9,
+            "warm_frac_of_peak": rbytes / (call_mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        if cow is not None:
+            line["copy_on_write"] = cow
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kernel_src, w.name),
                 "kernel": ("prefill_kernel key ranges (pa_decode_partials, pass 1 of pa_decode, "
                            "matrix-core route)" if on_mc else
                            "decode_partial_kernel (pa_decode_partials, pass 1 of pa_decode)"),
-                "algorithmic_bytes_per_launch": dbytes,
+                "algorithmic_bytes_per_launch": rbytes,
+                "bytes_counted": "each physical block once" if shared else "every sequence's keys",
                 "launch_us_mean": attn_mean_ms * 1e3, "launch_us_median": attn_median_ms * 1e3,
                 "pa_decode_call_us_mean": call_mean_ms * 1e3,
-                "pa_decode_call_achieved": dbytes / (call_mean_ms * 1e-3) / 1e9,
+                "pa_decode_call_achieved": rbytes / (call_mean_ms * 1e-3) / 1e9,
+                "pa_decode_call_frac": rbytes / (call_mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 "cold_launch_us_median": None if cold_median_ms is None else cold_median_ms * 1e3,
-                "cold_achieved": None if not cold_median_ms else dbytes / (cold_median_ms * 1e-3) / 1e9,
+                "cold_achieved": None if not cold_median_ms else rbytes / (cold_median_ms * 1e-3) / 1e9,
+                "cold_call_us_median": None if cold_call_median_ms is None else cold_call_median_ms * 1e3,
                 "attainable_stream_read": attainable,
                 "frac_of_attainable": achieved / attainable if attainable else None}
     else:
@@ -374,7 +522,15 @@ def main() -> int:
                 "algorithmic_flops_per_launch": fl, "launch_us_mean": attn_mean_ms * 1e3,
                 "launch_us_median": attn_median_ms * 1e3,
                 "cold_launch_us_median": None if cold_median_ms is None else cold_median_ms * 1e3,
+                "cold_achieved": None if not cold_median_ms else fl / (cold_median_ms * 1e-3) / 1e12,
                 "contiguous_kv": contiguous}
+        line["headline"] = {
+            "what": "pa_prefill_varlen call, L2 and MALL evicted before each call",
+            "us_median": None if cold_median_ms is None else cold_median_ms * 1e3,
+            "TFLOPs": None if not cold_median_ms else fl / (cold_median_ms * 1e-3) / 1e12,
+            "frac_of_peak": None if not cold_median_ms else
+            fl / (cold_median_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "warm_us_mean": attn_mean_ms * 1e3, "warm_frac_of_peak": achieved / BF16_MFMA_PEAK_TFLOPS}
         if contiguous:
             contiguous["achieved"] = fl / (contiguous["launch_us_mean"] * 1e-6) / 1e12
         if unsplit:
@@ -384,10 +540,7 @@ def main() -> int:
                  "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
                  "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
                  "config": cfg, "roofline": roof})
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    else:
-        line["cpu_baseline"] = None
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
     return 0
 

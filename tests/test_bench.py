@@ -56,3 +56,40 @@ def test_decode_bytes_count_every_byte_read_or_written():
         total += 4 * len({j // w.block_size for j in range(n)})   # one table entry per page
     total += w.batch * w.num_heads * w.head_dim * elem * 2       # q read, out written
     assert bench.decode_bytes(w, p) == total
+
+
+def test_unique_bytes_count_each_shared_slot_once():
+    # a small shared-prefix workload: every (physical block, slot) read by some sequence
+    # is counted once, against decode_bytes' once per sequence
+    w = W.shared_prefix_decode(seed=1, groups=2, per_group=3, prefix_len=48, suffix_lo=3,
+                               suffix_hi=30, block_size=16)
+    p = W.plan(w, OB.BlockManager, OB.slot_mapping, OB.cu_seqlens)
+    elem = 2
+    slots = set()
+    for b, n in enumerate(p.seqlens_k):
+        for j in range(n):
+            slots.add(OA.locate(p.tables[b], j, w.block_size))
+    pages = sum(len({j // w.block_size for j in range(n)}) for n in p.seqlens_k)
+    unique = (len(slots) * 2 * w.num_kv_heads * w.head_dim * elem
+              + w.batch * w.num_heads * w.head_dim * elem * 2 + 4 * pages)
+    assert bench.decode_unique_bytes(w, p) == unique
+    assert bench.decode_unique_bytes(w, p) < bench.decode_bytes(w, p)
+    # without sharing the two counts agree
+    w2 = W.decode_workload([30, 32, 70], dtype="bf16", seed=7)
+    p2 = W.plan(w2, OB.BlockManager, OB.slot_mapping, OB.cu_seqlens)
+    assert bench.decode_unique_bytes(w2, p2) == bench.decode_bytes(w2, p2)
+
+
+def test_cpu_baseline_reports_one_core_and_all_cores():
+    w = W.decode_workload([40, 70, 9, 33], dtype="bf16", num_heads=4, num_kv_heads=2,
+                          head_dim=64, block_size=16, seed=2)
+    cb = bench.cpu_baseline(w, 0.2)
+    for key in ("value", "value_all_cores", "value_1core", "cores", "cpu_model", "nproc"):
+        assert key in cb
+    assert cb["value"] == cb["value_all_cores"] > 0 and cb["value_1core"] > 0
+    assert len(cb["runs_all_cores"]) == len(cb["runs_1core"]) == 3
+    assert 1 <= cb["cores"] <= 16 and cb["unit"] == "GB/s"
+    wp = W.prefill_workload([5, 0], [70, 3], num_heads=4, num_kv_heads=2, head_dim=64,
+                            block_size=16, seed=4)
+    cp = bench.cpu_baseline(wp, 0.2)
+    assert cp["unit"] == "TFLOP/s" and cp["value"] > 0
