@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 
 HOST_SOURCES = ["host.cpp"]
-HIP_SOURCES = ["kv_write.hip", "decode.hip", "decode_groups.hip", "prefill.hip", "probe.hip"]
+HIP_SOURCES = ["kv_write.hip", "decode.hip", "decode_groups.hip", "prefill.hip", "prefill_k128.hip",
+               "prefill_k128_odd.hip", "prefill_k64.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
