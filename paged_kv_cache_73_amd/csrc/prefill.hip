@@ -35,23 +35,6 @@ constexpr int64_t kSplitTargetUnits = 1024;
 constexpr int64_t kMinSplitTiles = 1024 / kPrefillKeys;      // tiles of a range: 1024 keys
 constexpr int64_t kMinSplitTilesExact = 512 / kPrefillKeys;  // 512 keys
 
-// workgroup slots of the current device: two per CU (the prefill kernel's occupancy).
-// The CU count is read once per device (each device of a process has its own entry).
-inline int64_t prefill_slots() {
-    constexpr int kMaxDevices = 64;
-    static std::atomic<int32_t> cus_of[kMaxDevices];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    int cus = dev < kMaxDevices ? cus_of[dev].load(std::memory_order_relaxed) : 0;
-    if (cus <= 0) {
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-        if (dev < kMaxDevices) cus_of[dev].store(cus, std::memory_order_relaxed);
-    }
-    return 2 * static_cast<int64_t>(cus);
-}
-
 inline SplitPlan plan_split(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                             int32_t max_seqlen_q, int32_t max_seqlen_k, bool causal,
                             const int32_t* host_cu_q, const int32_t* host_cu_k) {

@@ -7,12 +7,14 @@
 // c = k_len - q_len cached tokens, query row t sees keys j <= c + t when causal.
 //
 // How (gfx950, bf16 in, fp32 accumulate):
-// * A workgroup is a job: 128 "rows" of one request and one KV head, a row being a
-//   (token, query head) pair with the G query heads of the KV head next to each other, so
-//   every K/V tile read serves all of them.  Two waves of 64 rows (two 32-row blocks)
-//   each, one wave per SIMD and two workgroups per CU: every K or V^T operand read from
-//   LDS feeds the products of both row blocks, which halves the LDS bytes per product
-//   against one 32-row block per wave.
+// * A job is 128 "rows" of one request and one KV head, a row being a (token, query
+//   head) pair with the G query heads of the KV head next to each other, so every K/V
+//   tile read serves all of them.  A workgroup of four waves (32 rows each) runs a list of
+//   jobs; two workgroups per CU put two waves on every SIMD.  A single wave issues at
+//   most one instruction every fourth cycle, which, with the softmax, the loads and the
+//   operand reads beside its products, would leave the matrix core idle half the time; a
+//   second wave issues while the first waits.  (The register file then holds 32 rows of
+//   O per wave, and each K or V^T operand read from LDS feeds one product.)
 // * Keys are walked in tiles of 32, FlashAttention-style ("结合nanovllm的FlashAttention和
 //   PagedAttention主要原理概述" 题目3): each tile is gathered through the block table into LDS,
 //   its scores are folded into the running (m, l, O) with the §11.2 rule, and O is
@@ -20,24 +22,24 @@
 // * Transposed products keep a query row inside one lane: S^T = K Q^T with
 //   v_mfma_f32_32x32x16_bf16 (A = a K row per lane from LDS, B = the lane's q row held in
 //   registers), so lane l holds 16 of the tile's scores for row l%32 (the other 16 sit in
-//   lane l^32).  O^T += V^T P^T takes P straight from the S^T accumulators: the key order
-//   inside each 16-key step is permuted the same way on both operands, and the loader
-//   stores V transposed in that order, so a V^T operand is 16 contiguous bytes.
+//   lane l^32).  O^T += V^T P^T takes P straight from the S^T accumulators; its V^T
+//   operand comes from V stored as it is in memory (key-major) through gfx950's
+//   transposing LDS read, in the key order in which the accumulators hold the weights.
+// * K and V tiles go from memory to LDS by direct loads (no registers, no LDS stores):
+//   each wave loads an 8-key slice of every tile, which lies in one page, so the page
+//   address is a scalar; loads bounded to the slice's valid keys return zeros past kv_end
+//   and for a block id outside the pool, so masked keys never bring NaN into a product.
+//   Masking sets scores past a row's limit (and of unassigned blocks) to -inf.
 // * Software pipeline, one barrier per tile: while the products of tile t+1's scores run,
 //   the wave computes tile t's weights on the vector unit (the two are independent, and
 //   one wave issues vector instructions while its matrix products execute), then the
-//   products of tile t's P V.  The tiles live in a ring of three LDS buffers: t is read
-//   for V, t+1 for K, t+2 is being written from registers, whose loads for t+3 are in
-//   flight.
+//   products of tile t's P V.  Four LDS stages: t (V read), t+1 (K read), and the loads
+//   of t+2 and t+3 in flight, two steps ahead of their use.
 // * Weights without a per-tile maximum: p = 2^(s*scale*log2e - m) against the row's
-//   reference m, which moves only on a rare slow path (the first tile a row sees, or a
-//   tile whose weights sum past 2^64).  The quotient sum(p v) / sum(p) does not depend on
-//   m, and the bound keeps every sum finite.  Row sums are taken from the bf16 weights
-//   that enter the products (v_dot2).
-// * Each wave stages a 16-key slice of every tile, which lies in one page, so the page
-//   address is a scalar; buffer loads bounded to the slice's valid keys return zeros past
-//   kv_end and for a block id outside the pool, so masked keys never bring NaN into a
-//   product.  Masking sets scores past a row's limit (and of unassigned blocks) to -inf.
+//   reference m, the row's maximum over the unit's first tile.  The quotient
+//   sum(p v) / sum(p) does not depend on m; a tile whose weights sum past 2^64 sends the
+//   unit down a slow path that recomputes it against exact row maxima.  Row sums are taken
+//   from the bf16 weights that enter the products (v_dot2).
 // * BS = 0 instantiates the same kernel for contiguous K/V (the varlen call without a
 //   block table): request i's keys are rows [cu_k[i], cu_k[i+1]) of packed
 //   [sum_k][Hkv][d] arrays, and only the loader's addressing differs.
@@ -53,13 +55,42 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t* lds_v4_ptr_t;
 
-constexpr int kPrefillWaves = 2;                          // waves per workgroup
-constexpr int kWaveRows = 64;                             // rows per wave (two 32-row blocks)
-constexpr int kPrefillRows = kPrefillWaves * kWaveRows;   // rows per workgroup (a job)
+template <int S> using Stage = std::integral_constant<int, S>;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at dst + 16 l.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, const uint16_t* dst,
+                                           int32_t voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(dst)), 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ lds_v4_ptr_t to_lds_v4(const uint16_t* p) {
+    return (lds_v4_ptr_t)(const_cast<uint16_t*>(p));
+}
+
+// Wait until at most N of this wave's vector-memory instructions are outstanding (they
+// complete in order), then the workgroup barrier.  Direct-to-LDS loads count there, so
+// a wave's own loads of a stage have landed once it passes; the barrier makes them
+// every wave's.  The compiler's own barrier would first wait for every load in flight;
+// this one keeps the later stages' loads flying.  (The memory clobber keeps LDS accesses
+// on their side of it.)
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+constexpr int kRowBlocks = 1;                            // 32-row blocks per wave
+constexpr int kWaveRows = 32 * kRowBlocks;                // rows per wave
+constexpr int kPrefillRows = 128;                         // rows per workgroup (a job)
+constexpr int kPrefillWaves = kPrefillRows / kWaveRows;   // waves per workgroup
+constexpr int kWavesPerSimd = 2 / kRowBlocks;             // resident waves per SIMD
 constexpr int kPrefillKeys = 32;                          // keys per tile
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
-constexpr int kPrefillStages = 3;                         // LDS tile buffers
+constexpr int kPrefillStages = 4;                         // LDS tile buffers
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X
 constexpr float kFastSumLimit = 18446744073709551616.f;  // 2^64: weights of a tile on the fast path
 constexpr int kMaxRankedRequests = 256;  // requests ordered by key count in-kernel
@@ -77,27 +108,19 @@ __host__ __device__ inline int split_count(int tiles, int n_split, int split_til
     return parts < n_split ? parts : n_split;
 }
 
-// Row of V^T dimension i in LDS.  Rows 8 apart would share banks when the loader writes
-// them (a thread writes the 8 dims of one 16-byte chunk); XOR-ing the low two bits with
-// bits 3-4 spreads them, and 16 consecutive dims (one operand read) stay conflict free.
-__device__ __forceinline__ int vt_row(int i) { return i ^ ((i >> 3) & 3); }
-
 constexpr bf16x2_t kOnes2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-
-// sched_group_barrier masks
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 
 // BS = 0: contiguous K/V.  kSplit: jobs may be cut into key ranges (n_split, split_tiles);
 // without it those arguments are ignored and the kernel is the plain one.
 template <int D, int G, int BS, bool kSplit>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void prefill_kernel(
     const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, const int32_t* __restrict__ block_table,
     uint16_t* __restrict__ out, int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks,
     int32_t max_blocks, float qscale, int32_t causal, int32_t n_qtiles, int32_t n_groups,
     int32_t n_split_arg, int32_t split_tiles_arg, float* __restrict__ part_o,
-    float2* __restrict__ part_ml) {
+    float2* __restrict__ part_ml, int32_t n_slots) {
     const int n_split = kSplit ? n_split_arg : 1;
     const int split_tiles = kSplit ? split_tiles_arg : 0;
     constexpr int BN = kPrefillKeys;
@@ -107,33 +130,48 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     constexpr int TOK = kPrefillRows / G;       // tokens per workgroup
     constexpr int KS = D / 16;                  // MFMA k-steps over the head dim
     constexpr int DB = D / 32;                  // 32-wide blocks of the head dim in O^T
+    constexpr int RB = kRowBlocks;
+    constexpr int NP = 8 * RB;                  // weight pairs per lane and tile
     constexpr int CHUNKS = D / 8;               // 16-byte pieces per K/V row
-    constexpr int SLICE = BN / kPrefillWaves;   // keys of a tile staged by each wave
-    constexpr int GPW = kWave / CHUNKS;         // key groups per wave
-    constexpr int KPT = SLICE / GPW;            // keys per loader thread: 4 (d 128), 2 (d 64)
-    static_assert(KPT == 2 || KPT == 4, "loader split");
+    constexpr int SLICE = BN / kPrefillWaves;   // keys of a tile loaded by each wave
+    static_assert(D == 64 || D == 128, "head dims");
     static_assert(PBS % SLICE == 0 && BN % PBS == 0, "a wave's keys lie in one page");
-    // LDS: K rows with a 16-byte pad (16 consecutive rows then cover all banks once, for
-    // the operand reads and the loader's writes alike); V^T rows of 32 keys, 16-byte pad
-    constexpr int KP = D + 8;                   // K row pitch (elements)
-    constexpr int VP = BN + 8;                  // V^T row pitch (elements)
-    constexpr int K_ELEMS = BN * KP;
-    constexpr int STAGE = K_ELEMS + D * VP;     // one tile buffer
-    __shared__ __align__(16) uint16_t lds[kPrefillStages * STAGE];
-    static_assert(2 * kMaxRankedRequests + kMaxRankedJobs <= K_ELEMS / 2,
-                  "the ranking tables fit in the first K tile buffer");
+    // LDS: four stages of a K and a V tile (BN key-major rows of D elements each), each
+    // its own array, so that the compiler's wait counts can tell the stages' loads apart
+    constexpr int TILE = BN * D;
+    static_assert(kPrefillStages == 4, "four stages");
+    __shared__ __align__(16) uint16_t k_st0[TILE], k_st1[TILE], k_st2[TILE], k_st3[TILE];
+    __shared__ __align__(16) uint16_t v_st0[TILE], v_st1[TILE], v_st2[TILE], v_st3[TILE];
+    auto k_of = [&](auto st) -> uint16_t* {
+        constexpr int S = decltype(st)::value;
+        if constexpr (S == 0) return k_st0; else if constexpr (S == 1) return k_st1;
+        else if constexpr (S == 2) return k_st2; else return k_st3;
+    };
+    auto v_of = [&](auto st) -> uint16_t* {
+        constexpr int S = decltype(st)::value;
+        if constexpr (S == 0) return v_st0; else if constexpr (S == 1) return v_st1;
+        else if constexpr (S == 2) return v_st2; else return v_st3;
+    };
+    static_assert((kMaxRankedRequests + kMaxRankedJobs) * 4 <= TILE * 2,
+                  "the ranking's scratch tables fit in the first K stage");
+    __shared__ int32_t perm[kMaxRankedRequests];   // request of each rank
+    __shared__ int32_t order[kMaxRankedJobs];      // this XCD's work unit of each rank
+    __shared__ int32_t redo;
 
-    // Work items are jobs (group, query tile), a group being one (request, KV head).
-    // Workgroup L runs on XCD L % 8 (workgroups are handed to the XCDs round-robin), and
-    // the jobs of group g all run on XCD g % 8: the query tiles of a group read the same
-    // K/V pages, which then stay in that XCD's L2.  Requests are ranked by key count,
-    // longest first, and group g belongs to the request of rank g / Hkv, so that every
-    // request's heads are spread over the 8 XCDs.  Within an XCD the jobs start in order
-    // of decreasing key-tile count (longest-processing-time first): workgroup slot s of
-    // the XCD takes the job of rank s, and the short jobs fill the gaps at the end.
-    // Every workgroup derives the same orders from cu_q / cu_k in LDS (the first tile
-    // buffer, overwritten only after a barrier); beyond kMaxRankedRequests requests or
-    // kMaxRankedJobs jobs per XCD the batch order is kept instead.
+    // Work units are jobs (group, query tile), a group being one (request, KV head), or
+    // key ranges of jobs when splitting.  Workgroup L runs on XCD L % 8 (workgroups are
+    // handed to the XCDs round-robin), and the jobs of group g all run on XCD g % 8: the
+    // query tiles of a group read the same K/V pages, which then stay in that XCD's L2.
+    // Requests are ranked by key count, longest first, and group g belongs to the
+    // request of rank g / Hkv, so that every request's heads are spread over the 8 XCDs.
+    // The grid holds n_slots workgroups per XCD (no more than can run at once), each of
+    // which runs a list of its XCD's units: they are ranked by key tiles, longest first,
+    // and dealt to the slots in snake order (round k gives rank kS + s, or kS + S-1-s in
+    // odd rounds, to slot s), so that the long units start first and each slot's short
+    // ones balance its long ones.  Workgroups started by the hardware as others end would
+    // wait for a slot on their own XCD; these never wait.  Every workgroup derives the
+    // same orders from cu_q / cu_k in LDS; beyond kMaxRankedRequests requests or
+    // kMaxRankedJobs units per XCD the batch order is kept instead.
     const int L = blockIdx.x;
     const int xcd = L % kXcds;
     const int slot = L / kXcds;
@@ -160,10 +198,8 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     };
     const bool rank_requests = batch > 1 && batch <= kMaxRankedRequests;
     const bool rank_jobs = n_jobs > 1 && n_jobs <= kMaxRankedJobs;
-    int32_t* const perm = reinterpret_cast<int32_t*>(lds);           // request of each rank
-    int32_t* const klen = perm + kMaxRankedRequests;                 // key count of each request
-    int32_t* const jobs = klen + kMaxRankedRequests;                 // key tiles of each job
-    __shared__ int32_t found;
+    int32_t* const klen = reinterpret_cast<int32_t*>(k_st0);  // key count of each request
+    int32_t* const jobs = klen + kMaxRankedRequests;             // sort key of each unit
     if (rank_requests) {
         const int padded = (batch + 3) & ~3;  // whole 16-byte reads; -1 pads (below any count)
         for (int j = tid; j < padded; j += kPrefillThreads)
@@ -186,14 +222,13 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         __syncthreads();
     }
     auto request_of = [&](int rank) { return rank_requests ? perm[rank] : rank; };
-    int group, qtile, split;
     if (rank_jobs) {
-        // job c of this XCD: group (c / n_qtiles) * 8 + xcd, query tile c % n_qtiles.  Its
-        // sort key packs the key tiles (+1, so that -1 for "no job" stays non-negative)
-        // above 0xFFFF - c, so that keys are distinct and a larger key means "earlier":
-        // more tiles, or as many and a lower index.  The rank of job c is the number of
-        // larger keys; the table is padded with zeros (below every key) to whole 16-byte
-        // reads.
+        // unit c of this XCD: job c / n_split (group (job / n_qtiles) * 8 + xcd, query
+        // tile job % n_qtiles), key range c % n_split.  Its sort key packs the key tiles
+        // (+1, so that -1 for "no unit" stays non-negative) above 0xFFFF - c, so that keys
+        // are distinct and a larger key means "earlier": more tiles, or as many and a lower
+        // index.  The rank of unit c is the number of larger keys; the table is padded
+        // with zeros (below every key) to whole 16-byte reads.
         const int padded = (n_jobs + 3) & ~3;
         for (int c = tid; c < padded; c += kPrefillThreads) {
             int32_t key = 0;
@@ -216,23 +251,18 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                 const int4 u = jobs4[i];
                 ahead += (u.x > v) + (u.y > v) + (u.z > v) + (u.w > v);
             }
-            if (ahead == slot) found = c;
+            order[ahead] = c;
         }
-        __syncthreads();
-        const int c = __builtin_amdgcn_readfirstlane(found);
-        const int job = c / n_split;
-        group = (job / n_qtiles) * kXcds + xcd;
-        qtile = job % n_qtiles;
-        split = c % n_split;
-    } else {
-        // the groups of the XCD in turn, the query tiles of a group back to back, the
-        // later ones (which see more keys under the causal mask) first, the key ranges
-        // of a job next to each other
-        const int job = slot / n_split;
-        group = (job / n_qtiles) * kXcds + xcd;
-        qtile = n_qtiles - 1 - job % n_qtiles;
-        split = slot % n_split;
+        __syncthreads();  // (the scratch tables in the first K stage are free after this)
     }
+
+    auto run_unit = [&](int c) {
+    const int job = c / n_split;
+    const int group = (job / n_qtiles) * kXcds + xcd;
+    // ranked: query tiles in index order; batch order: the later ones (which see more
+    // keys under the causal mask) first, the key ranges of a job next to each other
+    const int qtile = rank_jobs ? job % n_qtiles : n_qtiles - 1 - job % n_qtiles;
+    const int split = c % n_split;
     if (group >= n_groups) return;  // uniform: grid padding
     const int hkv = group % num_kv_heads;
     const int req = __builtin_amdgcn_readfirstlane(request_of(group / num_kv_heads));  // scalar addressing
@@ -260,10 +290,10 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     constexpr bool kAllRows = TOK * G == kPrefillRows;
     constexpr int kUsedRows = TOK * G;
     // the two rows of this lane: row block rb holds workgroup row 64w + 32rb + r
-    int tok[2], head[2], row_limit[2];
-    bool row_ok[2];
+    int tok[RB], head[RB], row_limit[RB];
+    bool row_ok[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const int row = kWaveRows * w + 32 * rb + r;
         tok[rb] = tok0 + row / G;
         head[rb] = hkv * G + row % G;
@@ -285,9 +315,9 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int t_end = max(t_lo, min(t_hi, wave_hi < 0 ? t_lo : wave_hi / BN + 1));
 
     // q rows of this lane, pieces 16s + 8h .. +8 of the head dim
-    bf16x8_t qf[2][KS];
+    bf16x8_t qf[RB][KS];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const uint16_t* qrow = q + (static_cast<int64_t>(q0 + tok[rb]) * num_heads + head[rb]) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -297,57 +327,78 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         }
     }
 
-    f32x16_t acc[2][DB];
+    f32x16_t acc[RB][DB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int x = 0; x < 16; ++x) acc[rb][db][x] = 0.f;
-    float m_ref[2] = {-INFINITY, -INFINITY};  // row reference (base 2, scaled); same in lanes l, l^32
-    float lsum[2] = {0.f, 0.f};               // this lane's part of the row sums
+    float m_ref[RB], lsum[RB];  // row reference (base 2, scaled; same in lanes l, l^32), this lane's part of the row sum
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m_ref[rb] = -INFINITY;
+        lsum[rb] = 0.f;
+    }
 
     const int32_t* table_row = kPaged ? block_table + static_cast<int64_t>(req) * max_blocks : nullptr;
     const int64_t key_base = kPaged ? 0 : cu_k[req];  // first packed row of the request (contiguous)
     const int32_t row_stride = num_kv_heads * D * 2;  // bytes per slot
 
-    // Loader.  Wave w stages keys [16w, 16w+16) of every tile; they lie in one page, so
-    // the page's address is a scalar and each thread's offsets inside it never change.
-    // Thread (c, g) of the wave loads chunk c (8 dims) of the KPT consecutive keys
-    // g*KPT .. g*KPT+KPT-1, which lets it transpose V on its own: for every dim, the KPT
-    // values are adjacent in a V^T row.  A buffer descriptor bounded to the wave's valid
-    // keys makes every other load return zeros (keys past kv_end, and the whole slice of
-    // a block id outside the pool), so nothing masked can be NaN.
-    const int lc = lane / GPW;            // chunk of the row
-    const int lg = lane % GPW;            // key group inside the wave's slice
-    int32_t voff[KPT];
+    // ---- loader ---------------------------------------------------------------------
+    // Tiles arrive in LDS by direct loads (buffer_load ... lds): a load instruction
+    // writes its 64 lanes' 16-byte pieces to 1 KB of LDS in lane order, so the loader
+    // picks, for every LDS slot, which piece of global memory lands there.  Wave w loads
+    // keys [8w, 8w+8) of every tile (they lie in one page: the page's address is a
+    // scalar and each lane's offsets inside it never change), KPI keys per instruction,
+    // K and V alike.  Rows are key-major, D elements each, and the 16-byte chunks of a
+    // row are permuted (an XOR of the chunk index with a function of the key), which
+    // keeps the operand reads below free of bank conflicts.  A buffer descriptor bounded
+    // to the slice's valid keys makes every other lane load zeros (keys past kv_end or
+    // past the unit, and the whole slice of a block id outside the pool), so nothing
+    // masked can be NaN.
+    constexpr int KPI = kWave * 16 / (2 * D);  // keys per load instruction: 4 (d 128), 8 (d 64)
+    constexpr int NIK = SLICE / KPI;           // K (and V) load instructions per wave and tile
+    constexpr int NL = 2 * NIK + (kPaged ? 1 : 0);  // vector-memory instructions per wave and tile
+    // chunk permutations.  K is read 16 keys x one chunk at a time (one chunk per lane):
+    // those must fall in 16 different 16-byte bank groups.  V is read transposed, 4 keys
+    // x 4 chunks at a time: the keys' 64 bytes must fall in different quarters of the
+    // 256-byte bank space.
+    auto swz_k = [](int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); };
+    auto swz_v = [](int key) { return D == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); };
+    int32_t voff_k[NIK], voff_v[NIK];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) voff[u] = (lg * KPT + u) * row_stride + lc * 16;
+    for (int j = 0; j < NIK; ++j) {
+        const int kl = KPI * j + lane / CHUNKS;  // key inside the wave's slice
+        const int kt = SLICE * w + kl;           // key inside the tile
+        const int p = lane % CHUNKS;             // LDS slot of the row
+        voff_k[j] = kl * row_stride + 16 * (p ^ swz_k(kt));
+        voff_v[j] = kl * row_stride + 16 * (p ^ swz_v(kt));
+    }
     const int64_t head_off = static_cast<int64_t>(hkv) * D * 2;
 
     // Block ids of a tile's pages come from one vector load (all lanes read the same
-    // words), issued with the K/V loads of the tile before, so the wait that precedes the
-    // LDS stores covers it (scalar loads would hold up the LDS waits, which share their
+    // words), issued two tiles ahead of the tile's own loads, so the wait that precedes
+    // them covers it (scalar loads would hold up the LDS waits, which share their
     // counter).  The words are moved to scalar registers when used.
     const __amdgpu_buffer_rsrc_t table_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int32_t*>(kPaged ? table_row : cu_k), 0, kPaged ? max_blocks * 4 : 0,
         kBufferDword3);
-    auto load_ids = [&](int t) -> u32x4 {  // ids of tile t's pages; zero past the table
+    auto load_ids = [&](int t) -> u32x2 {  // ids of tile t's pages; zero past the table
         const int off = t * PAGES * 4;
         if constexpr (!kPaged) {
-            return u32x4{0, 0, 0, 0};
+            return u32x2{0, 0};
         } else if constexpr (PAGES == 2) {
-            const auto x = __builtin_amdgcn_raw_buffer_load_b64(table_rsrc, off, 0, 0);
-            return u32x4{x[0], x[1], 0, 0};
+            return __builtin_amdgcn_raw_buffer_load_b64(table_rsrc, off, 0, 0);
         } else {
-            return u32x4{__builtin_amdgcn_raw_buffer_load_b32(table_rsrc, off, 0, 0), 0, 0, 0};
+            return u32x2{__builtin_amdgcn_raw_buffer_load_b32(table_rsrc, off, 0, 0), 0};
         }
     };
     struct TileIds {
         uint32_t bits;  // bit i: page i is past kv_end or holds a block id inside the pool
         int32_t wave;   // block id of this wave's slice
     };
-    auto scalar_ids = [&](int t, const u32x4& v) {
+    auto scalar_ids = [&](int t, const u32x2& v) {
         TileIds res{(1u << PAGES) - 1, 0};
         if constexpr (kPaged) {
             res.bits = 0;
@@ -361,90 +412,97 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         }
         return res;
     };
-    uint4 kr[KPT], vr[KPT];
-    auto fetch_into = [&](int t, int32_t id, uint4 (&kd)[KPT], uint4 (&vd)[KPT]) {
-        const int kw0 = t * BN + SLICE * w;                // first key of this wave's slice
-        const int nvalid = min(max(kv_end - kw0, 0), SLICE);
-        bool ok = nvalid > 0;
-        int64_t base;
+    // the loads of this wave's slice of tile t: their two descriptors (K, V), then the
+    // 2 NIK instructions one by one (issue), or all of them (load_tile)
+    struct TileRsrc {
+        __amdgpu_buffer_rsrc_t k, v;
+    };
+    // Constants of the descriptors: the slice's offset inside a page (tiles are whole
+    // pages or whole multiples of them) with the head, as base pointers; keys past
+    // unit_end (the unit's last tile or kv_end) load zeros.
+    const int unit_end = min(kv_end, t_hi * BN);
+    const int64_t slice_off = kPaged ? static_cast<int64_t>((SLICE * w) % PBS) * row_stride + head_off
+                                     : (key_base + SLICE * w) * row_stride + head_off;
+    const char* const k_slice = k_cache + slice_off;
+    const char* const v_slice = v_cache + slice_off;
+    const uint32_t step_bytes = (kPaged ? PBS : BN) * static_cast<uint32_t>(row_stride);  // per block id / tile
+    auto tile_rsrc = [&](int t, int32_t id) {
+        int32_t bytes = min(max(unit_end - (t * BN + SLICE * w), 0), SLICE) * row_stride;
+        uint32_t index = static_cast<uint32_t>(t);
         if constexpr (kPaged) {
-            ok = ok && static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks);
-            base = (static_cast<int64_t>(id) * PBS + kw0 % PBS) * row_stride + head_off;
-        } else {
-            base = (key_base + kw0) * row_stride + head_off;
+            const bool in_pool = static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks);
+            index = in_pool ? static_cast<uint32_t>(id) : 0u;
+            bytes = in_pool ? bytes : 0;
         }
-        if (!ok) base = 0;
-        // (readfirstlane: a value the compiler forms on the vector unit would otherwise turn
+        // (readfirstlane: values the compiler would form on the vector unit would turn
         // each load into a loop over lanes)
-        const int32_t bytes = __builtin_amdgcn_readfirstlane(ok ? nvalid * row_stride : 0);
-        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>(k_cache + base), 0, bytes, kBufferDword3);
-        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>(v_cache + base), 0, bytes, kBufferDword3);
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            kd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(krs, voff[u], 0, 0));
-            vd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(vrs, voff[u], 0, 0));
-        }
+        bytes = __builtin_amdgcn_readfirstlane(bytes);
+        index = __builtin_amdgcn_readfirstlane(index);
+        const uint64_t off = static_cast<uint64_t>(index) * step_bytes;
+        return TileRsrc{__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(k_slice + off), 0, bytes, kBufferDword3),
+                        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(v_slice + off), 0, bytes, kBufferDword3)};
     };
-    // registers -> LDS buffer b, in units: unit u < KPT stores K row u of this thread as it
-    // is; unit KPT + e stores dim 8lc + e of V^T: this thread's KPT keys at the position
-    // of their 4-key quad q in the group's order q0 q2 q1 q3 (the order in which the P^T
-    // operand holds them)
-    constexpr int kStageUnits = KPT + 8;
-    const int k_st = (SLICE * w + lg * KPT) * KP + lc * 8;
-    const int quad = (lg * KPT) / 4;
-    const int v_col = SLICE * w + (quad & 1) * 8 + (quad >> 1) * 4 + (lg * KPT) % 4;
-    auto stage_unit = [&](int b, int j, const uint4 (&ks_)[KPT], const uint4 (&vs_)[KPT]) {
-        uint16_t* const kb = lds + b * STAGE;
-        uint16_t* const vb = kb + K_ELEMS;
-        if (j < KPT) {
-            *reinterpret_cast<uint4*>(kb + k_st + j * KP) = ks_[j];
-            return;
-        }
-        const int e = j - KPT;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-        const int i = e / 2;
-        uint16_t* dst = vb + vt_row(lc * 8 + e) * VP + v_col;
-        const uint32_t p01 = __builtin_amdgcn_perm(word(vs_[1], i), word(vs_[0], i), sel);
-        if constexpr (KPT == 4) {
-            const uint32_t p23 = __builtin_amdgcn_perm(word(vs_[3], i), word(vs_[2], i), sel);
-            *reinterpret_cast<uint2*>(dst) = make_uint2(p01, p23);
-        } else {
-            *reinterpret_cast<uint32_t*>(dst) = p01;
-        }
+    auto issue = [&](auto st, const TileRsrc& rs, int j) {
+        if (j < NIK)
+            load_lds16(rs.k, k_of(st) + (SLICE * w + KPI * j) * D, voff_k[j]);
+        else
+            load_lds16(rs.v, v_of(st) + (SLICE * w + KPI * (j - NIK)) * D, voff_v[j - NIK]);
     };
-    auto stage_from = [&](int b, const uint4 (&ks_)[KPT], const uint4 (&vs_)[KPT]) {
+    auto load_tile = [&](auto st, int t, int32_t id) {
+        const TileRsrc rs = tile_rsrc(t, id);
 #pragma unroll
-        for (int j = 0; j < kStageUnits; ++j) stage_unit(b, j, ks_, vs_);
+        for (int j = 0; j < 2 * NIK; ++j) issue(st, rs, j);
     };
 
-    // MFMA operand reads.  K: key r of the tile, dims 16ks + 8h .. +8.  V^T: dim
-    // 32db + r, keys 16ks + 8h .. +8 in the permuted order.
-    const int k_rd = r * KP + 8 * h;
-    const int v_rd = K_ELEMS + vt_row(r) * VP + 8 * h;   // vt_row(32db + r) = 32db + vt_row(r)
-    auto read_k = [&](int b, int ks) {
-        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(lds + b * STAGE + k_rd + 16 * ks));
+    // ---- operand reads ----------------------------------------------------------------
+    // K (A operand of S^T = K Q^T): key r of the tile, dims 16ks + 8h .. +8, one 16-byte
+    // read per k-step.
+    int32_t k_rd[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_rd[ks] = r * D + 8 * ((2 * ks + h) ^ swz_k(r));
+    auto read_k = [&](auto st, int ks) {
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(k_of(st) + k_rd[ks]));
     };
-    auto read_v = [&](int b, int db, int ks) {
-        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(
-            lds + b * STAGE + v_rd + 32 * db * VP + 16 * ks));
+    // V^T (A operand of O^T += V^T P^T): for dims 32db + r, the 8 keys that the P^T
+    // operand holds at contraction positions 8h .. 8h+7 of k-step ks, which are keys
+    // 16ks + 4h + e and 16ks + 8 + 4h + e (e < 4; the order in which the S^T accumulators
+    // hold a lane's keys).  Two transposing reads (ds_read_b64_tr_b16) of 4 keys each: in
+    // every 16-lane group, lane 4e + q supplies the address of 4 consecutive dims of key e,
+    // and lane j receives dim j%4 of the 4 keys supplied by lanes 4e + (j%16)/4.  Lane
+    // s = 16g + 4e + q therefore points at key 4(g/2) + e (+8, +16ks), dims
+    // 32db + 16(g%2) + 4q.
+    int32_t v_rd[DB];
+    {
+        const int g = lane / 16, e = (lane / 4) % 4, q4 = lane % 4;
+        const int key = 4 * (g / 2) + e;  // swz_v depends on key bits that 16ks and 8 keep
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int chunk = 4 * db + 2 * (g % 2) + q4 / 2;
+            v_rd[db] = key * D + 8 * (chunk ^ swz_v(key)) + 4 * (q4 % 2);
+        }
+    }
+    auto read_v = [&](auto st, int db, int ks) {
+        const uint16_t* p = v_of(st) + v_rd[db] + 16 * ks * D;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(to_lds_v4(p));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(to_lds_v4(p + 8 * D));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
     // S^T of a tile: s[rb] accumulates keys 8(x/4) + 4h + x%4 of the tile for row block rb
-    auto zero_s = [&](f32x16_t (&s)[2]) {
+    auto zero_s = [&](f32x16_t (&s)[RB]) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int x = 0; x < 16; ++x) s[rb][x] = 0.f;
     };
-    auto qk = [&](int b, f32x16_t (&s)[2]) {
+    auto qk = [&](auto st, f32x16_t (&s)[RB]) {
         zero_s(s);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8_t a = read_k(b, ks);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][ks], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][ks], s[1], 0, 0, 0);
+            const bf16x8_t a = read_k(st, ks);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][ks], s[rb], 0, 0, 0);
         }
     };
     // References.  Each row's reference is the maximum of its scores in the unit's first
@@ -453,84 +511,109 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // score far above the reference shows as a tile's weight sum above 2^64 (or not
     // finite); the workgroup then flags the unit and computes it again, first the exact
     // row maxima (a pass over the scores alone), then the attention against them.
-    __shared__ int32_t redo;
-    // one of the 16 pair sums of a tile's weights (pair o: row block o / 8, k-step
-    // (o / 4) % 2, elements 2(o % 4), +1), into one of two partial sums per row block
-    auto pair_sum = [&](const bf16x8_t (&pb)[2][2], int o, float (&part)[2][2]) {
-        const int rb = o / 8, ks = (o / 4) % 2, e = 2 * (o % 4);
-        const bf16x2_t pp = {pb[rb][ks][e], pb[rb][ks][e + 1]};
-        part[rb][o % 2] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, part[rb][o % 2], false);
+    // A tile's 16 weights per lane and row block come in pairs: pair pr is elements e, e+1
+    // of the P^T operand pb[rb][hf] (hf = pr / 4RB, rb = (pr % 4RB) / 4, e = 2 (pr % 4)),
+    // from the accumulators 8hf + e, +1 of the scores of row block rb.  Their row sums go
+    // to two independent partial sums per row block.
+    auto weight_pair = [&](const f32x16_t (&sc)[RB], const float (&mu)[RB], int pr, bf16x8_t (&pb)[RB][2]) {
+        const int hf = pr / (4 * RB), rb = (pr % (4 * RB)) / 4, e = 2 * (pr % 4);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * hf + e], qscale, -mu[rb]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * hf + e + 1], qscale, -mu[rb]));
+        const bf16x2_t pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
+        pb[rb][hf][e] = pp[0];
+        pb[rb][hf][e + 1] = pp[1];
     };
-    // Tile t+1's score products (K from buffer b) with tile t's weights (scores sc) in
-    // between, in source order: per k-step, its two products, then a share of the weights
-    // (32 per lane over the KS steps).  sched_barrier(0) fences keep each share next to its
-    // products: the products run on the matrix cores while the wave issues the vector
-    // instructions.  Nothing here waits on a weight (the row sums, which would, are taken
-    // during the P V products), so the wave never stalls behind an exponential.
-    auto qk_softmax = [&](int b, const f32x16_t (&sc)[2], f32x16_t (&sn)[2], bf16x8_t (&pb)[2][2]) {
-        constexpr int VPC = 32 / KS;  // weights per k-step: 4 (d 128) or 8 (d 64)
+    auto pair_sum = [&](const bf16x8_t (&pb)[RB][2], int pr, float (&part)[RB][2]) {
+        const int hf = pr / (4 * RB), rb = (pr % (4 * RB)) / 4, e = 2 * (pr % 4);
+        const bf16x2_t pp = {pb[rb][hf][e], pb[rb][hf][e + 1]};
+        part[rb][pr % 2] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, part[rb][pr % 2], false);
+    };
+    // The weights' vector work is spread over the matrix products of the step so that no
+    // stretch of it outlasts the products it sits between: the first kQkPairs pairs (all
+    // of hf 0, which the first P V products need, and part of hf 1) between tile t+1's
+    // score products, the rest between the first half of tile t's P V products (those of
+    // hf 0), and the row sums between the second half.
+    constexpr int kQkPairs = 6 * RB;
+    constexpr int kAhead = 4;  // operand reads in flight ahead of their products
+    // Tile t+1's score products (K from stage st) with kQkPairs of tile t's weight pairs
+    // (scores sc) in between, in source order: per k-step, its two products, then a share
+    // of the pairs.  sched_barrier(0) fences keep each share next to its products: the
+    // products run on the matrix cores while the wave issues the vector instructions.
+    auto qk_softmax = [&](auto st, const f32x16_t (&sc)[RB], f32x16_t (&sn)[RB], const float (&mu)[RB],
+                          bf16x8_t (&pb)[RB][2], auto lst, const TileRsrc& rs) {
         zero_s(sn);
-        const float mu[2] = {m_ref[0], m_ref[1]};
         bf16x8_t a[KS];
-        a[0] = read_k(b, 0);
-        a[1] = read_k(b, 1);
+#pragma unroll
+        for (int ks = 0; ks < kAhead; ++ks) a[ks] = read_k(st, ks);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 2 < KS) a[ks + 2] = read_k(b, ks + 2);
-            sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[0][ks], sn[0], 0, 0, 0);
-            sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[1][ks], sn[1], 0, 0, 0);
+            if (ks + kAhead < KS) a[ks + kAhead] = read_k(st, ks + kAhead);
+            // the next loads, spread over the k-steps (2 NIK instructions: one or two per step)
 #pragma unroll
-            for (int v = ks * VPC; v < (ks + 1) * VPC; v += 2) {
-                const int rb = v / 16, x = v % 16;
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[rb][x], qscale, -mu[rb]));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[rb][x + 1], qscale, -mu[rb]));
-                const bf16x2_t pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
-                pb[rb][x / 8][x % 8] = pp[0];
-                pb[rb][x / 8][x % 8 + 1] = pp[1];
-            }
+            for (int j = 2 * NIK * ks / KS; j < 2 * NIK * (ks + 1) / KS; ++j) issue(lst, rs, j);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                sn[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[rb][ks], sn[rb], 0, 0, 0);
+#pragma unroll
+            for (int pr = kQkPairs * ks / KS; pr < kQkPairs * (ks + 1) / KS; ++pr) weight_pair(sc, mu, pr, pb);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // Tile t's P V products (V^T from buffer b) with the staging of tile t+2 into buffer
-    // b2 in between: per operand read, its two products, then a share of the LDS stores.
-    // The row sums of the weights are taken here too, two independent partial sums per row
-    // block; a tile whose sums are not finite and at most 2^64 (a score far above its row's
+    // Tile t's P V products (V^T from stage st): per operand, its products, then a share
+    // of the remaining weight pairs (first half) or of the row sums (second half); mid()
+    // (scalar work of the loader) runs next to the second operand's products.
+    // A tile whose sums are not finite and at most 2^64 (a score far above its row's
     // reference) flags the unit to be computed again against exact row maxima.
-    auto pv_stage = [&](int b, const bf16x8_t (&pb)[2][2], int b2) {
+    auto pv = [&](auto st, const f32x16_t (&sc)[RB], const float (&mu)[RB], bf16x8_t (&pb)[RB][2], auto&& mid) {
         constexpr int NO = 2 * DB;  // V^T operands of a tile
-        float part[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+        constexpr int H = NO / 2;   // operands of one k-step
+        float part[RB][2];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) part[rb][0] = part[rb][1] = 0.f;
         bf16x8_t va[NO];
-        va[0] = read_v(b, 0, 0);
-        va[1] = read_v(b, 1 % DB, 1 / DB);
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) va[i] = read_v(st, i % DB, i / DB);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NO; ++i) {
             const int ks = i / DB, db = i % DB;
-            if (i + 2 < NO) va[i + 2] = read_v(b, (i + 2) % DB, (i + 2) / DB);
-            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[0][ks], acc[0][db], 0, 0, 0);
-            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[1][ks], acc[1][db], 0, 0, 0);
+            if (i + kAhead < NO) va[i + kAhead] = read_v(st, (i + kAhead) % DB, (i + kAhead) / DB);
 #pragma unroll
-            for (int j = i; j < kStageUnits; j += NO) stage_unit(b2, j, kr, vr);
+            for (int rb = 0; rb < RB; ++rb)
+                acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[rb][ks], acc[rb][db], 0, 0, 0);
+            if (i < H) {
 #pragma unroll
-            for (int o = i; o < 16; o += NO) pair_sum(pb, o, part);
+                for (int pr = kQkPairs + (NP - kQkPairs) * i / H; pr < kQkPairs + (NP - kQkPairs) * (i + 1) / H; ++pr)
+                    weight_pair(sc, mu, pr, pb);
+            } else {
+#pragma unroll
+                for (int pr = NP * (i - H) / H; pr < NP * (i - H + 1) / H; ++pr) pair_sum(pb, pr, part);
+            }
+            if (i == 1) mid();
             __builtin_amdgcn_sched_barrier(0);
         }
-        const float ps0 = part[0][0] + part[0][1], ps1 = part[1][0] + part[1][1];
-        lsum[0] += ps0;
-        lsum[1] += ps1;
-        if (!(ps0 <= kFastSumLimit) || !(ps1 <= kFastSumLimit)) redo = 1;
+        bool over = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float ps = part[rb][0] + part[rb][1];
+            lsum[rb] += ps;
+            over = over || !(ps <= kFastSumLimit);
+        }
+        if (over) redo = 1;
     };
 
     // masking of tile t: keys past a row's limit, keys of an unassigned block (none
     // in most tiles: the caller tests need_mask first)
+    // (tile t has a key past wave_lo iff t >= t_mask)
+    const int t_mask = (wave_lo + 1) / BN;  // wave_lo >= -1
     auto need_mask = [&](int t, uint32_t page_ok) {
-        return page_ok != (1u << PAGES) - 1 || t * BN + BN - 1 > wave_lo;
+        return page_ok != (1u << PAGES) - 1 || t >= t_mask;
     };
-    auto mask = [&](int t, f32x16_t (&s)[2], uint32_t page_ok) {
+    auto mask = [&](int t, f32x16_t (&s)[RB], uint32_t page_ok) {
         const int j0 = t * BN;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
             const int lim = row_limit[rb] - j0 - 4 * h;  // keys 8(x/4) + x%4 <= lim are visible
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
@@ -542,7 +625,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             // accumulator x holds key 8(x/4) + 4h + x%4, in page (8(x/4)) / PBS for both lane
             // halves: a compile-time index
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int x = 0; x < 16; ++x) {
                     const int page = (8 * (x / 4)) / PBS;
@@ -550,27 +633,10 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                 }
         }
     };
-    // weights of a tile against the current references: P^T operands pb[rb][ks] (keys of
-    // k-step ks: accumulators 8ks .. 8ks+7).  Their row sums are taken with the P V
-    // products (pv_stage), from the rounded weights that enter them.
-    auto weights = [&](const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][8 * ks + e], qscale, -m_ref[rb]));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][8 * ks + e + 1], qscale, -m_ref[rb]));
-                    const bf16x2_t pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
-                    pb[rb][ks][e] = pp[0];
-                    pb[rb][ks][e + 1] = pp[1];
-                }
-    };
     // row maxima of a tile's scores (scaled to base 2; lanes l and l^32 agree)
-    auto tile_max = [&](const f32x16_t (&s)[2], float (&mx)[2]) {
+    auto tile_max = [&](const f32x16_t (&s)[RB], float (&mx)[RB]) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
             float v = -INFINITY;
 #pragma unroll
             for (int x = 0; x < 16; ++x) v = fmaxf(v, s[rb][x]);
@@ -581,128 +647,135 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // the end
     auto pin_acc = [&]() {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[rb][db]));
     };
 
     // ---- the key loop ---------------------------------------------------------------
     // One pass over the unit's tiles: the attention (MAX_ONLY false), or the row maxima
-    // of the scores alone into m_ref (MAX_ONLY true).  Staging and loads run every
-    // iteration: past the unit's last tile they load zeros (the descriptors' bounds) into
-    // a buffer nobody reads.  The tiles this wave computes come first, two per loop trip
-    // so that the two sets of score registers alternate without copies; the last one has
-    // no next tile's products; tiles past the wave's rows (if any) are only staged.
+    // of the scores alone into m_ref (MAX_ONLY true).  Four LDS stages: at step t the
+    // wave computes tile t+1's scores (stage of t+1) and tile t's P V (stage of t), while
+    // the loads of tiles t+2 and t+3 are in flight, so a load has two steps to land.
+    // Step t starts by waiting for its own loads of tile t+1 (all but the last step's
+    // NL vector-memory instructions) and a barrier, after which tile t+1 is complete in
+    // LDS and every wave is done with tile t-1's stage, into which tile t+3 is then
+    // loaded.  The stage of a tile is fixed by its position in the unit, so the loop is
+    // unrolled four times and every LDS address is static.  Both waves run every step
+    // (the loads and barriers are shared); a wave computes only tiles before its t_end.
     const int n = t_hi - t_lo;
     auto key_pass = [&](auto max_only, bool set_refs) {
         constexpr bool MAX_ONLY = decltype(max_only)::value;
-        uint32_t okq = 0;  // page bits of tiles t, t+1, t+2, t+3 at bits 0, 2, 4, 6
-        u32x4 ids_next = u32x4{0, 0, 0, 0};
-        f32x16_t sa[2], sb[2];
         if (n <= 0) return;
+        uint32_t okq;   // page bits of tiles t .. t+4 at bits 0, 2, 4, 6, 8
+        u32x2 ids[2];   // block ids in flight (tiles t+4 and t+5 at step t)
+        TileRsrc rs3;   // descriptors of the loads of tile t+3 at step t
+        f32x16_t sa[RB], sb[RB];
+        // scores are read by vector instructions: keep them in vector registers
+        auto pin_s = [&](f32x16_t (&s)[RB]) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) asm volatile("" : "+v"(s[rb]));
+        };
         {
-            // the first two tiles' ids, then their loads, in flight together
-            const u32x4 id0 = load_ids(t_lo), id1 = load_ids(t_lo + 1);
-            const TileIds first = scalar_ids(t_lo, id0), second = scalar_ids(t_lo + 1, id1);
-            uint4 kr1[KPT], vr1[KPT];
-            fetch_into(t_lo, first.wave, kr, vr);
-            fetch_into(t_lo + 1, second.wave, kr1, vr1);
-            ids_next = load_ids(t_lo + 2);
-            okq = first.bits | (second.bits << 2);
+            const u32x2 i0 = load_ids(t_lo), i1 = load_ids(t_lo + 1), i2 = load_ids(t_lo + 2),
+                        i3 = load_ids(t_lo + 3);
             __syncthreads();  // LDS of the job orders or of the pass before: no longer read
-            stage_from(0, kr, vr);
-            stage_from(1, kr1, vr1);
-            const TileIds t2 = scalar_ids(t_lo + 2, ids_next);
-            fetch_into(t_lo + 2, t2.wave, kr, vr);
-            okq |= t2.bits << 4;
-            ids_next = load_ids(t_lo + 3);
-            __syncthreads();
+            const TileIds a0 = scalar_ids(t_lo, i0), a1 = scalar_ids(t_lo + 1, i1),
+                          a2 = scalar_ids(t_lo + 2, i2), a3 = scalar_ids(t_lo + 3, i3);
+            load_tile(Stage<0>{}, t_lo, a0.wave);
+            load_tile(Stage<1>{}, t_lo + 1, a1.wave);
+            load_tile(Stage<2>{}, t_lo + 2, a2.wave);
+            ids[1] = load_ids(t_lo + 4);
+            rs3 = tile_rsrc(t_lo + 3, a3.wave);
+            okq = a0.bits | (a1.bits << 2) | (a2.bits << 4) | (a3.bits << 6);
+            wait_loads_and_barrier<4 * NIK + (kPaged ? 1 : 0)>();  // tile t_lo in LDS (the later loads may fly)
             if (t_lo < t_end) {
-                qk(0, sa);
-                asm volatile("" : "+v"(sa[0]), "+v"(sa[1]));
+                qk(Stage<0>{}, sa);
+                pin_s(sa);
                 if (!MAX_ONLY && set_refs) {
                     if (need_mask(t_lo, okq & 3u)) mask(t_lo, sa, okq & 3u);
-                    float mx[2];
+                    float mx[RB];
                     tile_max(sa, mx);
-                    m_ref[0] = mx[0] == -INFINITY ? 0.f : mx[0];
-                    m_ref[1] = mx[1] == -INFINITY ? 0.f : mx[1];
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) m_ref[rb] = mx[rb] == -INFINITY ? 0.f : mx[rb];
                 }
             }
-            if (!MAX_ONLY && set_refs && t_lo >= t_end) m_ref[0] = m_ref[1] = 0.f;
+            if (!MAX_ONLY && set_refs && t_lo >= t_end) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) m_ref[rb] = 0.f;
+            }
         }
-        int b = 0;  // buffer of tile t
-        // the loads of tile t+3 (after tile t+2 left the registers for LDS)
-        auto fetch_next = [&](int t) {
-            const TileIds ti = scalar_ids(t + 3, ids_next);
-            fetch_into(t + 3, ti.wave, kr, vr);
-            okq |= ti.bits << 6;
-            ids_next = load_ids(t + 4);
-        };
-        auto advance = [&]() {
-            __syncthreads();
-            okq >>= 2;
-            b = b == kPrefillStages - 1 ? 0 : b + 1;
-        };
-        // one computed tile t (scores in sc); NEXT: tile t+1's score products into sn
-        auto step = [&](int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2], auto next) {
-            constexpr bool NEXT = decltype(next)::value;
-            const int b1 = b == kPrefillStages - 1 ? 0 : b + 1;
-            const int b2 = b == 0 ? kPrefillStages - 1 : b - 1;
-            if (need_mask(t, okq & 3u)) mask(t, sc, okq & 3u);
-            if constexpr (MAX_ONLY) {
-                float mx[2];
-                tile_max(sc, mx);
-                m_ref[0] = fmaxf(m_ref[0], mx[0]);
-                m_ref[1] = fmaxf(m_ref[1], mx[1]);
-                if constexpr (NEXT) qk(b1, sn);
-                stage_from(b2, kr, vr);
-            } else {
-                bf16x8_t pb[2][2];
-                if constexpr (NEXT) {
-                    qk_softmax(b1, sc, sn, pb);
-                } else {
-                    weights(sc, pb);
-                }
-                pv_stage(b, pb, b2);
-                pin_acc();
+        // Step t: tile t in stage ST, its scores in sc; tile t+1's go to sn.  The loads of
+        // tile t+3 (descriptors made at step t-1) are issued between the score products;
+        // the block ids of tile t+5 are loaded; the descriptors of tile t+4 are made from
+        // its ids (loaded at step t-1) between the P V products.
+        auto step = [&](auto st, int t, f32x16_t (&sc)[RB], f32x16_t (&sn)[RB], u32x2& ids_new,
+                        const u32x2& ids_t4) {
+            constexpr int ST = decltype(st)::value;
+            wait_loads_and_barrier<NL>();
+            const TileRsrc rs = rs3;
+            ids_new = load_ids(t + 5);
+            auto next_desc = [&]() {
+                const TileIds ti = scalar_ids(t + 4, ids_t4);
+                rs3 = tile_rsrc(t + 4, ti.wave);
+                okq |= ti.bits << 8;
+            };
+            constexpr auto lst = Stage<(ST + 3) % 4>{};
+            if (MAX_ONLY || !(t < t_end)) {
+#pragma unroll
+                for (int j = 0; j < 2 * NIK; ++j) issue(lst, rs, j);
             }
-            fetch_next(t);
-            // the next tile's scores are read by vector instructions: keep them in vector
-            // registers (placed after the products of both tiles, so that it does not split
-            // the stretch above)
-            if constexpr (NEXT) asm volatile("" : "+v"(sn[0]), "+v"(sn[1]));
-            advance();
+            if (t < t_end) {
+                if (need_mask(t, okq & 3u)) mask(t, sc, okq & 3u);
+                if constexpr (MAX_ONLY) {
+                    float mx[RB];
+                    tile_max(sc, mx);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) m_ref[rb] = fmaxf(m_ref[rb], mx[rb]);
+                    qk(Stage<(ST + 1) % 4>{}, sn);
+                    next_desc();
+                } else {
+                    bf16x8_t pb[RB][2];
+                    float mu[RB];
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) mu[rb] = m_ref[rb];
+                    qk_softmax(Stage<(ST + 1) % 4>{}, sc, sn, mu, pb, lst, rs);
+                    pv(Stage<ST>{}, sc, mu, pb, next_desc);
+                    pin_acc();
+                }
+                // (placed after the products, so that it does not split the stretch above)
+                pin_s(sn);
+            } else {
+                next_desc();
+            }
+            okq >>= 2;
         };
         int t = t_lo;
-        for (; t + 2 < t_end; t += 2) {
-            step(t, sa, sb, std::true_type{});
-            step(t + 1, sb, sa, std::true_type{});
+        for (; t + 4 <= t_hi; t += 4) {
+            step(Stage<0>{}, t, sa, sb, ids[0], ids[1]);
+            step(Stage<1>{}, t + 1, sb, sa, ids[1], ids[0]);
+            step(Stage<2>{}, t + 2, sa, sb, ids[0], ids[1]);
+            step(Stage<3>{}, t + 3, sb, sa, ids[1], ids[0]);
         }
-        if (t + 1 < t_end) {
-            step(t, sa, sb, std::true_type{});
-            step(t + 1, sb, sa, std::false_type{});
-            t += 2;
-        } else if (t < t_end) {
-            step(t, sa, sb, std::false_type{});
-            t += 1;
-        }
-        for (; t < t_hi; ++t) {
-            stage_from(b == 0 ? kPrefillStages - 1 : b - 1, kr, vr);
-            fetch_next(t);
-            advance();
-        }
+        if (t < t_hi) step(Stage<0>{}, t, sa, sb, ids[0], ids[1]);
+        if (t + 1 < t_hi) step(Stage<1>{}, t + 1, sb, sa, ids[1], ids[0]);
+        if (t + 2 < t_hi) step(Stage<2>{}, t + 2, sa, sb, ids[0], ids[1]);
+        // the loads past the unit land before the stages are used again (or the wave ends)
+        wait_loads_and_barrier<0>();
     };
     if (tid == 0) redo = 0;  // (seen by every wave after the pass's first barrier)
     pin_acc();
     key_pass(std::false_type{}, true);
     __syncthreads();  // every wave's flag is in
-    if (redo) {       // uniform: the same LDS word for the whole workgroup
+    const bool again = redo != 0;  // uniform: the same LDS word for the whole workgroup
+    __syncthreads();  // every wave has read it (the next unit clears it)
+    if (again) {
         // exact row maxima first, then the attention against them (no weight exceeds 1)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) m_ref[rb] = -INFINITY;
+        for (int rb = 0; rb < RB; ++rb) m_ref[rb] = -INFINITY;
         key_pass(std::true_type{}, false);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
             m_ref[rb] = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
             lsum[rb] = 0.f;
 #pragma unroll
@@ -716,7 +789,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 
     // normalise and store: lane holds d = 32db + 8i + 4h + jj of its rows
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const float lt = lsum[rb] + __shfl_xor(lsum[rb], 32);
         const int row = kWaveRows * w + 32 * rb + r;
         if (kSplit && n_split_job > 1) {
@@ -749,6 +822,14 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                               (static_cast<uint32_t>(to_bf16_bits(acc[rb][db][4 * i4 + 3] * inv)) << 16);
                 *reinterpret_cast<uint2*>(orow + 32 * db + 8 * i4 + 4 * h) = make_uint2(lo, hi);
             }
+    }
+    };  // run_unit
+
+    // this slot's units, dealt in snake order from the XCD's ranking
+    for (int k = 0;; ++k) {
+        const int rank = k * n_slots + (k % 2 == 0 ? slot : n_slots - 1 - slot);
+        if (rank >= n_jobs) break;  // (the last round: no later one)
+        run_unit(rank_jobs ? order[rank] : rank);
     }
 }
 

@@ -4,6 +4,9 @@
 // they compile in parallel) and by prefill.hip, which plans and routes the calls.
 #pragma once
 
+#include <algorithm>
+#include <atomic>
+
 #include "prefill_kernel.h"
 
 namespace pa {
@@ -108,6 +111,23 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(
 
 // The varlen prefill run token by token on the decode kernel (decode.hip): the path
 
+// Workgroups of the prefill kernel that run at once: two per CU (LDS and registers),
+// counted per device on first use.
+inline int64_t prefill_slots() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int32_t> cus_of[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int cus = dev < kMaxDevices ? cus_of[dev].load(std::memory_order_relaxed) : 0;
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        if (dev < kMaxDevices) cus_of[dev].store(cus, std::memory_order_relaxed);
+    }
+    return 2 * static_cast<int64_t>(cus);
+}
+
 template <int D, int G, int BS>
 int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                    int32_t num_heads, const int32_t* cu_q, const int32_t* cu_k,
@@ -116,12 +136,13 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
     const int tok_per_wg = kPrefillRows / G;
     const int64_t n_qtiles = (max_seqlen_q + tok_per_wg - 1) / tok_per_wg;
     const int64_t n_groups = static_cast<int64_t>(kv.num_kv_heads) * batch;
-    const int64_t padded = (n_groups + kXcds - 1) / kXcds * n_qtiles * sp.n_split * kXcds;
-    if (padded > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    const int64_t per_xcd = (n_groups + kXcds - 1) / kXcds * n_qtiles * sp.n_split;  // work units
+    if (per_xcd * kXcds > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    const int32_t n_slots = static_cast<int32_t>(std::max<int64_t>(1, std::min(per_xcd, prefill_slots() / kXcds)));
     float* part_o = sp.n_split > 1 ? static_cast<float*>(workspace) : nullptr;
     float2* part_ml = sp.n_split > 1
         ? reinterpret_cast<float2*>(part_o + static_cast<size_t>(sp.units) * kPrefillRows * D) : nullptr;
-    const dim3 grid(static_cast<uint32_t>(padded));
+    const dim3 grid(static_cast<uint32_t>(n_slots * kXcds));
     if (!(passes & kPass1)) {
         // the merge alone (of ranges stored by an earlier call)
     } else if (sp.n_split > 1)
@@ -131,7 +152,7 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                            static_cast<uint16_t*>(out), num_heads, kv.num_kv_heads,
                            kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
                            static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups),
-                           sp.n_split, sp.split_tiles, part_o, part_ml);
+                           sp.n_split, sp.split_tiles, part_o, part_ml, n_slots);
     else
         hipLaunchKernelGGL((prefill_kernel<D, G, BS, false>), grid, dim3(kPrefillThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const char*>(kv.k),
@@ -139,7 +160,7 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                            static_cast<uint16_t*>(out), num_heads, kv.num_kv_heads,
                            kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
                            static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups), 1, 0,
-                           nullptr, nullptr);
+                           nullptr, nullptr, n_slots);
     if (sp.n_split > 1 && (passes & kPass2)) {
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
         // workgroups per job: the rows of the tokens a query tile can hold (one token per
