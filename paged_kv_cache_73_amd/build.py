@@ -25,7 +25,17 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
+# The prefill kernel keeps O, the scores and the operands in vector registers (two waves
+# per SIMD leave each 256 of them): matrix products write their results there directly.
+PREFILL_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCE_FLAGS = {"prefill_k128.hip": PREFILL_FLAGS, "prefill_k128_odd.hip": PREFILL_FLAGS,
+                "prefill_k64.hip": PREFILL_FLAGS}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
+
+def hip_flags(src: str) -> list[str]:
+    """hipcc flags of one HIP source."""
+    return [*HIPCC_FLAGS, *SOURCE_FLAGS.get(src, [])]
 
 
 def _hipcc() -> str:
@@ -51,7 +61,7 @@ def build(verbose: bool = False) -> str:
         jobs.append(["g++", *CXX_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src),
                      "-o", os.path.join(OBJ, src + ".o")])
     for src in HIP_SOURCES:
-        jobs.append([hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+        jobs.append([hipcc, *hip_flags(src), "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, src), "-o", os.path.join(OBJ, src + ".o")])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         results = list(ex.map(_run, jobs))

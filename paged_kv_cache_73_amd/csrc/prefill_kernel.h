@@ -643,13 +643,13 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             mx[rb] = fmaxf(v, __shfl_xor(v, 32)) * qscale;  // qscale > 0: the max scales with it
         }
     };
-    // O stays in the accumulation registers: nothing but the products touches it until
-    // the end
+    // O stays in vector registers, where the products accumulate it: nothing else touches
+    // it until the end
     auto pin_acc = [&]() {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[rb][db]));
+            for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(acc[rb][db]));
     };
 
     // ---- the key loop ---------------------------------------------------------------
