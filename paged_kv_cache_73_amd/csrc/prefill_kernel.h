@@ -377,34 +377,33 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     }
     const int64_t head_off = static_cast<int64_t>(hkv) * D * 2;
 
-    // Block ids of a tile's pages come from one vector load (all lanes read the same
-    // words), issued two tiles ahead of the tile's own loads, so the wait that precedes
-    // them covers it (scalar loads would hold up the LDS waits, which share their
-    // counter).  The words are moved to scalar registers when used.
+    // Block ids of the pages of four tiles at a time come from one vector load (lane i
+    // holds page i of them), issued four tiles ahead of their use (scalar loads would
+    // hold up the LDS waits, which share their counter); a tile's ids are moved to scalar
+    // registers when its loads are prepared.
     const __amdgpu_buffer_rsrc_t table_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int32_t*>(kPaged ? table_row : cu_k), 0, kPaged ? max_blocks * 4 : 0,
         kBufferDword3);
-    auto load_ids = [&](int t) -> u32x2 {  // ids of tile t's pages; zero past the table
-        const int off = t * PAGES * 4;
+    auto load_idq = [&](int t0) -> uint32_t {  // ids of tiles [t0, t0+4); zero past the table
         if constexpr (!kPaged) {
-            return u32x2{0, 0};
-        } else if constexpr (PAGES == 2) {
-            return __builtin_amdgcn_raw_buffer_load_b64(table_rsrc, off, 0, 0);
+            return 0u;
         } else {
-            return u32x2{__builtin_amdgcn_raw_buffer_load_b32(table_rsrc, off, 0, 0), 0};
+            const int i = lane < 4 * PAGES ? lane : 0;  // (other lanes: a copy of lane 0's word)
+            return __builtin_amdgcn_raw_buffer_load_b32(table_rsrc, (t0 * PAGES + i) * 4, 0, 0);
         }
     };
     struct TileIds {
         uint32_t bits;  // bit i: page i is past kv_end or holds a block id inside the pool
         int32_t wave;   // block id of this wave's slice
     };
-    auto scalar_ids = [&](int t, const u32x2& v) {
+    // ids of tile t, the k-th tile of the four in idq
+    auto scalar_ids = [&](int t, uint32_t idq, int k) {
         TileIds res{(1u << PAGES) - 1, 0};
         if constexpr (kPaged) {
             res.bits = 0;
 #pragma unroll
             for (int i = 0; i < PAGES; ++i) {
-                const int32_t id = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(v[i]));
+                const int32_t id = __builtin_amdgcn_readlane(static_cast<int32_t>(idq), k * PAGES + i);
                 const bool past = t * BN + i * PBS >= kv_end;
                 res.bits |= (past || static_cast<uint32_t>(id) < static_cast<uint32_t>(num_blocks) ? 1u : 0u) << i;
                 if ((SLICE * w) / PBS == i) res.wave = id;
@@ -667,9 +666,10 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     auto key_pass = [&](auto max_only, bool set_refs) {
         constexpr bool MAX_ONLY = decltype(max_only)::value;
         if (n <= 0) return;
-        uint32_t okq;   // page bits of tiles t .. t+4 at bits 0, 2, 4, 6, 8
-        u32x2 ids[2];   // block ids in flight (tiles t+4 and t+5 at step t)
-        TileRsrc rs3;   // descriptors of the loads of tile t+3 at step t
+        uint32_t okq;      // page bits of tiles t .. t+4 at bits 0, 2, 4, 6, 8
+        uint32_t idq_cur;  // block ids of tiles [t0+4, t0+8), t0 the first tile of the loop trip
+        uint32_t idq_next; // those of [t0+8, t0+12), loaded during the trip
+        TileRsrc rs3;      // descriptors of the loads of tile t+3 at step t
         f32x16_t sa[RB], sb[RB];
         // scores are read by vector instructions: keep them in vector registers
         auto pin_s = [&](f32x16_t (&s)[RB]) {
@@ -677,18 +677,17 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             for (int rb = 0; rb < RB; ++rb) asm volatile("" : "+v"(s[rb]));
         };
         {
-            const u32x2 i0 = load_ids(t_lo), i1 = load_ids(t_lo + 1), i2 = load_ids(t_lo + 2),
-                        i3 = load_ids(t_lo + 3);
+            const uint32_t q0 = load_idq(t_lo);
+            idq_cur = load_idq(t_lo + 4);
             __syncthreads();  // LDS of the job orders or of the pass before: no longer read
-            const TileIds a0 = scalar_ids(t_lo, i0), a1 = scalar_ids(t_lo + 1, i1),
-                          a2 = scalar_ids(t_lo + 2, i2), a3 = scalar_ids(t_lo + 3, i3);
+            const TileIds a0 = scalar_ids(t_lo, q0, 0), a1 = scalar_ids(t_lo + 1, q0, 1),
+                          a2 = scalar_ids(t_lo + 2, q0, 2), a3 = scalar_ids(t_lo + 3, q0, 3);
             load_tile(Stage<0>{}, t_lo, a0.wave);
             load_tile(Stage<1>{}, t_lo + 1, a1.wave);
             load_tile(Stage<2>{}, t_lo + 2, a2.wave);
-            ids[1] = load_ids(t_lo + 4);
             rs3 = tile_rsrc(t_lo + 3, a3.wave);
             okq = a0.bits | (a1.bits << 2) | (a2.bits << 4) | (a3.bits << 6);
-            wait_loads_and_barrier<4 * NIK + (kPaged ? 1 : 0)>();  // tile t_lo in LDS (the later loads may fly)
+            wait_loads_and_barrier<4 * NIK>();  // tile t_lo in LDS (the later loads may fly)
             if (t_lo < t_end) {
                 qk(Stage<0>{}, sa);
                 pin_s(sa);
@@ -705,18 +704,18 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                 for (int rb = 0; rb < RB; ++rb) m_ref[rb] = 0.f;
             }
         }
-        // Step t: tile t in stage ST, its scores in sc; tile t+1's go to sn.  The loads of
-        // tile t+3 (descriptors made at step t-1) are issued between the score products;
-        // the block ids of tile t+5 are loaded; the descriptors of tile t+4 are made from
-        // its ids (loaded at step t-1) between the P V products.
-        auto step = [&](auto st, int t, f32x16_t (&sc)[RB], f32x16_t (&sn)[RB], u32x2& ids_new,
-                        const u32x2& ids_t4) {
+        // Step t (the ST-th of its loop trip): tile t in stage ST, its scores in sc; tile
+        // t+1's go to sn.  The loads of tile t+3 (descriptors made at step t-1) are issued
+        // between the score products, the descriptors of tile t+4 made between the P V
+        // products; the first step of a trip loads the block ids of the trip after next.
+        // A step issues 2 NIK loads, the first of a trip one more (after its tile loads),
+        // which fixes how many of them the next step's wait leaves in flight.
+        auto step = [&](auto st, int t, f32x16_t (&sc)[RB], f32x16_t (&sn)[RB]) {
             constexpr int ST = decltype(st)::value;
-            wait_loads_and_barrier<NL>();
+            wait_loads_and_barrier<2 * NIK + (ST == 1 && kPaged ? 1 : 0)>();
             const TileRsrc rs = rs3;
-            ids_new = load_ids(t + 5);
             auto next_desc = [&]() {
-                const TileIds ti = scalar_ids(t + 4, ids_t4);
+                const TileIds ti = scalar_ids(t + 4, idq_cur, ST);
                 rs3 = tile_rsrc(t + 4, ti.wave);
                 okq |= ti.bits << 8;
             };
@@ -724,6 +723,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             if (MAX_ONLY || !(t < t_end)) {
 #pragma unroll
                 for (int j = 0; j < 2 * NIK; ++j) issue(lst, rs, j);
+                if constexpr (ST == 0) idq_next = load_idq(t + 8);
             }
             if (t < t_end) {
                 if (need_mask(t, okq & 3u)) mask(t, sc, okq & 3u);
@@ -740,6 +740,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) mu[rb] = m_ref[rb];
                     qk_softmax(Stage<(ST + 1) % 4>{}, sc, sn, mu, pb, lst, rs);
+                    if constexpr (ST == 0) idq_next = load_idq(t + 8);
                     pv(Stage<ST>{}, sc, mu, pb, next_desc);
                     pin_acc();
                 }
@@ -752,14 +753,15 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         };
         int t = t_lo;
         for (; t + 4 <= t_hi; t += 4) {
-            step(Stage<0>{}, t, sa, sb, ids[0], ids[1]);
-            step(Stage<1>{}, t + 1, sb, sa, ids[1], ids[0]);
-            step(Stage<2>{}, t + 2, sa, sb, ids[0], ids[1]);
-            step(Stage<3>{}, t + 3, sb, sa, ids[1], ids[0]);
+            step(Stage<0>{}, t, sa, sb);
+            step(Stage<1>{}, t + 1, sb, sa);
+            step(Stage<2>{}, t + 2, sa, sb);
+            step(Stage<3>{}, t + 3, sb, sa);
+            idq_cur = idq_next;
         }
-        if (t < t_hi) step(Stage<0>{}, t, sa, sb, ids[0], ids[1]);
-        if (t + 1 < t_hi) step(Stage<1>{}, t + 1, sb, sa, ids[1], ids[0]);
-        if (t + 2 < t_hi) step(Stage<2>{}, t + 2, sa, sb, ids[0], ids[1]);
+        if (t < t_hi) step(Stage<0>{}, t, sa, sb);
+        if (t + 1 < t_hi) step(Stage<1>{}, t + 1, sb, sa);
+        if (t + 2 < t_hi) step(Stage<2>{}, t + 2, sa, sb);
         // the loads past the unit land before the stages are used again (or the wave ends)
         wait_loads_and_barrier<0>();
     };
