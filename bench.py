@@ -299,49 +299,62 @@ def main() -> int:
         attend()
     torch.cuda.synchronize()
 
-    # Events on the kernels' stream: decode brackets its first pass (the kernel that reads
-    # every K/V byte) and the whole call; prefill the call (one kernel).
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    # Events on the kernels' stream, around exactly one library call each: the whole
+    # attention call of the step (pa_decode: both passes and the gap between them;
+    # pa_prefill_varlen: one kernel), then, for decode, its first pass alone (the kernel
+    # that reads every K/V byte, which the roofline line is about).  The write of the
+    # step's new rows runs before each, outside the events.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, mid, b in ev:
+    for a, b in ev:
         R.write(w, r)
         a.record(stream)
-        if w.kind == "decode":
-            R.attend_partials(w, r, P)
-            mid.record(stream)
-            R.attend_merge(w, r, P)
-        else:
-            attend()
-            mid.record(stream)
+        attend()
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = sorted(a.elapsed_time(mid) for a, mid, b in ev)
-    call_ms = [a.elapsed_time(b) for a, mid, b in ev]
-    attn_mean_ms = sum(attn_ms) / len(attn_ms)
-    attn_median_ms = attn_ms[len(attn_ms) // 2]
+    call_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = wall * 1e3 / args.steps
 
-    # the same attention call after evicting L2 and the MALL by reading 1 GiB (a read
-    # leaves clean lines, so the timed call pays no write-backs)
-    flush = torch.ones(1 << 29, dtype=torch.float32, device=dev)
-    cold, cold_call = [], []
-    for _ in range(args.cold_reps):
-        flush.sum()
-        a, mid, b = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        a.record(stream)
+    def pass1():
         if w.kind == "decode":
             R.attend_partials(w, r, P)
-            mid.record(stream)
-            R.attend_merge(w, r, P)
         else:
             attend()
-            mid.record(stream)
-        b.record(stream)
+
+    if w.kind == "decode":
+        for a, b in ev:
+            R.write(w, r)
+            a.record(stream)
+            pass1()
+            b.record(stream)
         torch.cuda.synchronize()
-        cold.append(a.elapsed_time(mid))
-        cold_call.append(a.elapsed_time(b))
+        attn_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    else:
+        attn_ms = sorted(call_ms)
+    attn_mean_ms = sum(attn_ms) / len(attn_ms)
+    attn_median_ms = attn_ms[len(attn_ms) // 2]
+
+    # the same calls after evicting L2 and the MALL by reading 1 GiB (a read leaves clean
+    # lines, so the timed call pays no write-backs)
+    flush = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+
+    def cold_times(fn):
+        out = []
+        for _ in range(args.cold_reps):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return out
+
+    cold_call = cold_times(attend)
+    cold = cold_times(pass1) if w.kind == "decode" else cold_call
     # attainable read bandwidth: plain streaming read of 2 GiB (best of a few grids)
     import paged_kv_cache_73_amd as pa
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -448,7 +461,8 @@ def main() -> int:
     on_mc = (w.kind == "decode" and w.dtype == "bf16" and w.head_dim in (64, 128)
              and w.block_size in (16, 32) and (5 <= group <= 8 or group in (16, 32)))
     kernel_src = ([os.path.join(csrc, "decode_kernel.h"), os.path.join(csrc, "decode.hip")]
-                  if w.kind == "decode" and not on_mc else [os.path.join(csrc, "prefill.hip")])
+                  if w.kind == "decode" and not on_mc else
+                  [os.path.join(csrc, f) for f in ("prefill_kernel.h", "prefill_launch.h", "prefill.hip")])
     cfg = {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
            "num_blocks": w.num_blocks, "seed": args.seed}
