@@ -153,6 +153,26 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
               void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * pa_decode_noalloc: pa_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The split-K scratch is a static device array of the library,
+ * PA_DECODE_SCRATCH_BYTES on each GPU it runs on, held until the process ends; the call
+ * allocates nothing and frees nothing.  Arguments, results and the other errors as for
+ * pa_decode.
+ * Errors: PA_ERR_WORKSPACE when the call would need more scratch than the array holds
+ *   (pa_decode_workspace_bytes(...) > PA_DECODE_SCRATCH_BYTES for these arguments),
+ *   checked before any launch; PA_ERR_HIP when the array's address cannot be had.
+ * Calls on one GPU share its array: calls that overlap on one GPU (other streams, other
+ *   threads) race and must not be made; calls in order on one stream are fine.
+ * ------------------------------------------------------------------------------- */
+#define PA_DECODE_SCRATCH_BYTES (16u << 20)
+
+int pa_decode_noalloc(const pa_kv_pool* pool, void* out, const void* q, int32_t batch,
+                      int32_t num_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* seqlens_k, int32_t max_seqlen_k, float softmax_scale,
+                      int32_t partition_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * The two passes of pa_decode as separate calls (split-K decoding: partial states per
  * partition, then their merge by the [PA11] §11.2 rule), for callers that schedule
  * them apart or time them apart.  pa_decode_partials takes pa_decode's arguments plus

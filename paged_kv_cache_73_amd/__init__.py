@@ -6,9 +6,9 @@ keep their C names.  See :mod:`paged_kv_cache_73_amd._native`.
 """
 
 from ._native import (  # noqa: F401
-    EXPORTS, BlockManager, KVPool, OutOfBlocks, PaError, RefcountError, lib,
+    EXPORTS, PA_DECODE_SCRATCH_BYTES, BlockManager, KVPool, OutOfBlocks, PaError, RefcountError, lib,
     pa_abi_version, pa_build_cu_seqlens, pa_build_slot_mapping, pa_copy_blocks, pa_decode,
-    pa_decode_append, pa_decode_merge, pa_decode_partials, pa_decode_workspace_bytes, pa_pool_bytes, pa_prefill_varlen,
+    pa_decode_append, pa_decode_merge, pa_decode_noalloc, pa_decode_partials, pa_decode_workspace_bytes, pa_pool_bytes, pa_prefill_varlen,
     pa_prefill_varlen_contiguous, pa_prefill_varlen_splitk, pa_prefill_workspace_bytes,
     pa_prefix_block_hash,
     pa_probe_stream_read, pa_status_str,

@@ -20,6 +20,9 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "P
           -4: "PA_ERR_HIP", -5: "PA_ERR_OUT_OF_BLOCKS", -6: "PA_ERR_REFCOUNT",
           -7: "PA_ERR_METADATA"}
 
+# bytes of the static device scratch of pa_decode_noalloc (PA_DECODE_SCRATCH_BYTES of pa.h)
+PA_DECODE_SCRATCH_BYTES = 16 << 20
+
 # every symbol include/pa.h declares
 EXPORTS = [
     "pa_status_str", "pa_abi_version", "pa_write_kv", "pa_copy_blocks",
@@ -30,7 +33,7 @@ EXPORTS = [
     "pa_validate_decode", "pa_validate_varlen", "pa_validate_slots", "pa_probe_stream_read",
     "pa_prefix_block_hash", "pa_bm_allocate_prefix", "pa_decode_append",
     "pa_prefill_varlen_contiguous", "pa_decode_partials", "pa_decode_merge",
-    "pa_prefill_workspace_bytes", "pa_prefill_varlen_splitk",
+    "pa_prefill_workspace_bytes", "pa_prefill_varlen_splitk", "pa_decode_noalloc",
 ]
 
 
@@ -86,6 +89,8 @@ def lib() -> ctypes.CDLL:
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7),
         "pa_decode": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP, _I32, _VP,
                                      _I32, ctypes.c_float, _I32, _VP, ctypes.c_size_t, _VP]),
+        "pa_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _I32, _VP, _I32,
+                                             _VP, _I32, ctypes.c_float, _I32, _VP]),
         "pa_decode_append": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _VP, _VP, _I32, _I32, _VP,
                                             _I32, _VP, _I32, ctypes.c_float, _I32, _VP,
                                             ctypes.c_size_t, _VP]),
@@ -246,6 +251,17 @@ def pa_decode(pool: KVPool, out, q, block_table, seqlens_k, max_seqlen_k: int,
                          _stream(stream))
     if st:
         _raise(st, "pa_decode")
+
+
+def pa_decode_noalloc(pool: KVPool, out, q, block_table, seqlens_k, max_seqlen_k: int,
+                      softmax_scale: float, partition_tokens: int = 0, stream=None) -> None:
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    st = lib().pa_decode_noalloc(ctypes.byref(pool.struct), _dev(out, "out"), _dev(q, "q"), batch,
+                                 hq, _meta(block_table, "block_table"), int(block_table.shape[1]),
+                                 _meta(seqlens_k, "seqlens_k"), int(max_seqlen_k),
+                                 float(softmax_scale), int(partition_tokens), _stream(stream))
+    if st:
+        _raise(st, "pa_decode_noalloc")
 
 
 def pa_decode_append(pool: KVPool, out, q, k_new, v_new, block_table, seqlens_k,

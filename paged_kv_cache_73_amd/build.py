@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libpa.so")
 
 HOST_SOURCES = ["host.cpp"]
 HIP_SOURCES = ["kv_write.hip", "decode.hip", "decode_groups.hip", "prefill.hip", "prefill_k128.hip",
-               "prefill_k128_odd.hip", "prefill_k64.hip", "probe.hip"]
+               "prefill_k128_odd.hip", "prefill_k64.hip", "probe.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -27,6 +27,9 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(L, name), name
     assert pa.pa_abi_version() == 1
+    # the binding's copy of the no-alloc scratch size is the header's
+    m = re.search(r"#define PA_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", header)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.PA_DECODE_SCRATCH_BYTES
     assert pa.pa_status_str(-5) == "PA_ERR_OUT_OF_BLOCKS"
     assert pa.pa_status_str(12345) == "PA_ERR_UNKNOWN"
 
