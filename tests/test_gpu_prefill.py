@@ -523,3 +523,20 @@ def test_prefill_many_requests(batch, q_hi, num_heads, num_kv_heads):
     w = W.prefill_workload(cached, new, num_heads=num_heads, num_kv_heads=num_kv_heads,
                            head_dim=64, block_size=16, seed=33)
     _run(w, requests=list(range(0, batch, 7)))
+
+
+@pytest.mark.parametrize("per_key", [1.0, -1.0])
+def test_prefill_recompute_in_every_unit_of_a_workgroup(per_key):
+    # Many small requests (about three jobs per workgroup slot, each workgroup running a
+    # list of them) whose scores rise by 1 per key: from the third key tile on, a tile's
+    # weights outgrow the first tile's reference, so every job takes the recompute path
+    # (exact row maxima, then the attention again) before its workgroup's next job.
+    # Falling scores: the first tile holds every maximum, no recompute.  All rows checked.
+    rng = random.Random(77)
+    batch = 640
+    new = [rng.randint(1, 8) for _ in range(batch)]
+    cached = [rng.randint(64, 160) for _ in range(batch)]
+    w = W.prefill_workload(cached, new, num_heads=4, num_kv_heads=2, head_dim=64,
+                           block_size=16, seed=35)
+    H.score_ramp(w, per_key)
+    _run(w)
