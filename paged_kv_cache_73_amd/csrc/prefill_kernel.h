@@ -571,6 +571,10 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) part[rb][0] = part[rb][1] = 0.f;
         bf16x8_t va[NO];
+        // Raised priority over these products: when both waves of the SIMD can issue,
+        // this wave's products go first and run back to back on the matrix core, and the
+        // other wave's vector work (its weights) takes the slots in between.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) va[i] = read_v(st, i % DB, i / DB);
         __builtin_amdgcn_sched_barrier(0);
@@ -592,6 +596,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             if (i == 1) mid();
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         bool over = false;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
