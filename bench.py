@@ -299,24 +299,32 @@ def main() -> int:
         attend()
     torch.cuda.synchronize()
 
-    # Events on the kernels' stream, around exactly one library call each: the whole
-    # attention call of the step (pa_decode: both passes and the gap between them;
-    # pa_prefill_varlen: one kernel), then, for decode, its first pass alone (the kernel
-    # that reads every K/V byte, which the roofline line is about).  The write of the
-    # step's new rows runs before each, outside the events.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # The timed region: exactly args.steps steps (the write of the step's new rows, then
+    # the attention call) and nothing else on the stream, between two synchronizes.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        R.write(w, r)
+        attend()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Then the same steps again with events on the kernels' stream around exactly one
+    # library call each (an event between two launches delays the second, so these are
+    # kept out of the timed region): the whole attention call of the step (pa_decode: both
+    # passes and the gap between them; pa_prefill_varlen: one kernel), then, for decode,
+    # its first pass alone (the kernel that reads every K/V byte, which the roofline line
+    # is about).  The write of the step's new rows runs before each, outside the events.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     for a, b in ev:
         R.write(w, r)
         a.record(stream)
         attend()
         b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     call_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = wall * 1e3 / args.steps
 
     def pass1():
         if w.kind == "decode":
@@ -401,16 +409,19 @@ def main() -> int:
     if w.kind == "decode":
         for _ in range(args.warmup):
             R.step(w, r, P, fused=True)
-        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        for _ in range(args.steps):
+            R.step(w, r, P, fused=True)
+        torch.cuda.synchronize()
+        fwall = time.perf_counter() - t1
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
         for a, b in fev:
             a.record(stream)
             R.step(w, r, P, fused=True)
             b.record(stream)
         torch.cuda.synchronize()
-        fwall = time.perf_counter() - t1
         fms = sorted(a.elapsed_time(b) for a, b in fev)
         fused = {"ms_per_step": fwall * 1e3 / args.steps,
                  "launch_us_mean": 1e3 * sum(fms) / len(fms),
