@@ -11,6 +11,6 @@ from ._native import (  # noqa: F401
     pa_decode_append, pa_decode_merge, pa_decode_noalloc, pa_decode_partials, pa_decode_workspace_bytes, pa_pool_bytes, pa_prefill_varlen,
     pa_prefill_varlen_contiguous, pa_prefill_varlen_splitk, pa_prefill_workspace_bytes,
     pa_prefix_block_hash,
-    pa_probe_stream_read, pa_status_str,
+    pa_probe_stream_read, pa_source_digest, pa_status_str,
     pa_validate_decode, pa_validate_slots, pa_validate_varlen, pa_write_kv,
 )

@@ -25,7 +25,7 @@ PA_DECODE_SCRATCH_BYTES = 16 << 20
 
 # every symbol include/pa.h declares
 EXPORTS = [
-    "pa_status_str", "pa_abi_version", "pa_write_kv", "pa_copy_blocks",
+    "pa_status_str", "pa_abi_version", "pa_source_digest", "pa_write_kv", "pa_copy_blocks",
     "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_varlen",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_free_stack",
     "pa_bm_alloc", "pa_bm_incref", "pa_bm_decref", "pa_bm_release_table", "pa_bm_share",
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_abi_version": (_I32, []),
+        "pa_source_digest": (ctypes.c_char_p, []),
         "pa_write_kv": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _VP, _I32, _VP]),
         "pa_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_Pool), _VP, _VP, _I32, _VP]),
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [_I32] * 7),
@@ -215,6 +216,10 @@ def pa_status_str(code: int) -> str:
 
 def pa_abi_version() -> int:
     return lib().pa_abi_version()
+
+
+def pa_source_digest() -> str:
+    return lib().pa_source_digest().decode()
 
 
 def pa_write_kv(pool: KVPool, k_new, v_new, slot_mapping, stream=None) -> None:

@@ -3,6 +3,7 @@ gfx950, linked by hipcc into paged_kv_cache_73_amd/libpa.so."""
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -33,6 +34,23 @@ SOURCE_FLAGS = {"prefill_k128.hip": PREFILL_FLAGS, "prefill_k128_odd.hip": PREFI
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 
+def source_digest() -> str:
+    """Digest of what the library is built from: include/pa.h, every file of csrc/ (path
+    and bytes, in name order) and the compile flags.  The build stores it in the library
+    (pa_source_digest), so that a prebuilt libpa.so can be checked against its sources."""
+    h = hashlib.sha256()
+    files = [os.path.join(INCLUDE, "pa.h")] + sorted(
+        os.path.join(CSRC, f) for f in os.listdir(CSRC)
+        if f.endswith((".hip", ".h", ".cpp")))
+    for path in files:
+        h.update(os.path.relpath(path, ROOT).encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    h.update(repr((HIPCC_FLAGS, sorted(SOURCE_FLAGS.items()), CXX_FLAGS)).encode())
+    return h.hexdigest()[:16]
+
+
 def hip_flags(src: str) -> list[str]:
     """hipcc flags of one HIP source."""
     return [*HIPCC_FLAGS, *SOURCE_FLAGS.get(src, [])]
@@ -57,9 +75,10 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     hipcc = _hipcc()
     jobs = []
+    digest = source_digest()
     for src in HOST_SOURCES:
-        jobs.append(["g++", *CXX_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src),
-                     "-o", os.path.join(OBJ, src + ".o")])
+        jobs.append(["g++", *CXX_FLAGS, f'-DPA_SOURCE_DIGEST="{digest}"', "-I", INCLUDE, "-c",
+                     os.path.join(CSRC, src), "-o", os.path.join(OBJ, src + ".o")])
     for src in HIP_SOURCES:
         jobs.append([hipcc, *hip_flags(src), "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, src), "-o", os.path.join(OBJ, src + ".o")])

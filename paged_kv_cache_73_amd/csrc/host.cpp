@@ -68,6 +68,11 @@ const char* pa_status_str(int status) {
 
 int32_t pa_abi_version(void) { return 1; }
 
+#ifndef PA_SOURCE_DIGEST
+#define PA_SOURCE_DIGEST "unknown"
+#endif
+const char* pa_source_digest(void) { return PA_SOURCE_DIGEST; }
+
 int pa_bm_create(int32_t num_blocks, const int32_t* initial_order, pa_bm** out) {
     if (out == nullptr || num_blocks < 0) return PA_ERR_INVALID_ARG;
     *out = nullptr;

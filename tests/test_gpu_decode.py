@@ -39,6 +39,14 @@ def _check_decode(w, partition_tokens=0, rows=None, what=""):
     return g, o
 
 
+def test_gpu_tests_run_the_library_built_from_these_sources():
+    """The libpa.so this GPU run loads carries the digest of the sources it was built
+    from; it equals the digest of this tree's header, csrc/ and flags, so every GPU test
+    here exercises a binary of exactly these sources."""
+    from paged_kv_cache_73_amd import build as B
+    assert pa.pa_source_digest() == B.source_digest()
+
+
 # --------------------------------------------------------------------------------------
 # KV write and copy-on-write: bit-exact
 # --------------------------------------------------------------------------------------

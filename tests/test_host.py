@@ -34,6 +34,14 @@ def test_library_exports_every_declared_symbol():
     assert pa.pa_status_str(12345) == "PA_ERR_UNKNOWN"
 
 
+def test_library_was_built_from_these_sources():
+    """The loaded libpa.so carries the digest of the sources it was built from; it must be
+    the digest of the header, csrc/ and flags in this tree (a stale or foreign binary
+    fails here rather than being tested in place of these sources)."""
+    from paged_kv_cache_73_amd import build as B
+    assert pa.pa_source_digest() == B.source_digest()
+
+
 
 def test_library_block_manager_reproduces_prefix_example(golden):
     g = golden("prefix_refcount_example.json")
