@@ -527,76 +527,60 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         const bf16x2_t pp = {pb[rb][hf][e], pb[rb][hf][e + 1]};
         part[rb][pr % 2] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, part[rb][pr % 2], false);
     };
-    // The weights' vector work is spread over the matrix products of the step so that no
-    // stretch of it outlasts the products it sits between: the first kQkPairs pairs (all
-    // of hf 0, which the first P V products need, and part of hf 1) between tile t+1's
-    // score products, the rest between the first half of tile t's P V products (those of
-    // hf 0), and the row sums between the second half.
-    constexpr int kQkPairs = 6 * RB;
+    // A step in two phases (two waves per SIMD): first its 16 products back to back (tile
+    // t+1's scores, then tile t's P V) at raised priority, then tile t+1's weights and row
+    // sums at normal priority.  The wave in its products keeps the matrix core busy while
+    // the other wave of the SIMD issues its vector work; the matrix core, which the two
+    // share, makes them take turns.  (Weights spread between the products of the same
+    // wave, or no priority, measured slower.)
     constexpr int kAhead = 4;  // operand reads in flight ahead of their products
-    // Tile t+1's score products (K from stage st) with kQkPairs of tile t's weight pairs
-    // (scores sc) in between, in source order: per k-step, its two products, then a share
-    // of the pairs.  sched_barrier(0) fences keep each share next to its products: the
-    // products run on the matrix cores while the wave issues the vector instructions.
-    auto qk_softmax = [&](auto st, const f32x16_t (&sc)[RB], f32x16_t (&sn)[RB], const float (&mu)[RB],
-                          bf16x8_t (&pb)[RB][2], auto lst, const TileRsrc& rs) {
+    // The products: tile t+1's scores (K from stage sk) and tile t's P V (V^T from stage
+    // sv).  The loads of tile t+3 (2 NIK instructions) are issued between the score
+    // products, the first kAhead V^T reads during the last score k-steps (so the first P V
+    // product finds its operand in), and mid() (scalar work of the loader) next to the
+    // second P V product; sched_barrier(0) fences keep that order.
+    auto products = [&](auto sk, auto sv, f32x16_t (&sn)[RB], const bf16x8_t (&pb)[RB][2], auto lst,
+                        const TileRsrc& rs, auto&& mid) {
+        constexpr int NO = 2 * DB;
         zero_s(sn);
         bf16x8_t a[KS];
+        bf16x8_t va[NO];
 #pragma unroll
-        for (int ks = 0; ks < kAhead; ++ks) a[ks] = read_k(st, ks);
+        for (int ks = 0; ks < kAhead; ++ks) a[ks] = read_k(sk, ks);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + kAhead < KS) a[ks + kAhead] = read_k(st, ks + kAhead);
-            // the next loads, spread over the k-steps (2 NIK instructions: one or two per step)
+            if (ks + kAhead < KS) a[ks + kAhead] = read_k(sk, ks + kAhead);
+            else va[ks + kAhead - KS] = read_v(sv, (ks + kAhead - KS) % DB, (ks + kAhead - KS) / DB);
 #pragma unroll
             for (int j = 2 * NIK * ks / KS; j < 2 * NIK * (ks + 1) / KS; ++j) issue(lst, rs, j);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 sn[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[rb][ks], sn[rb], 0, 0, 0);
-#pragma unroll
-            for (int pr = kQkPairs * ks / KS; pr < kQkPairs * (ks + 1) / KS; ++pr) weight_pair(sc, mu, pr, pb);
             __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    // Tile t's P V products (V^T from stage st): per operand, its products, then a share
-    // of the remaining weight pairs (first half) or of the row sums (second half); mid()
-    // (scalar work of the loader) runs next to the second operand's products.
-    // A tile whose sums are not finite and at most 2^64 (a score far above its row's
-    // reference) flags the unit to be computed again against exact row maxima.
-    auto pv = [&](auto st, const f32x16_t (&sc)[RB], const float (&mu)[RB], bf16x8_t (&pb)[RB][2], auto&& mid) {
-        constexpr int NO = 2 * DB;  // V^T operands of a tile
-        constexpr int H = NO / 2;   // operands of one k-step
-        float part[RB][2];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) part[rb][0] = part[rb][1] = 0.f;
-        bf16x8_t va[NO];
-        // Raised priority over these products: when both waves of the SIMD can issue,
-        // this wave's products go first and run back to back on the matrix core, and the
-        // other wave's vector work (its weights) takes the slots in between.
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) va[i] = read_v(st, i % DB, i / DB);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NO; ++i) {
             const int ks = i / DB, db = i % DB;
-            if (i + kAhead < NO) va[i + kAhead] = read_v(st, (i + kAhead) % DB, (i + kAhead) / DB);
+            if (i + kAhead < NO) va[i + kAhead] = read_v(sv, (i + kAhead) % DB, (i + kAhead) / DB);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[rb][ks], acc[rb][db], 0, 0, 0);
-            if (i < H) {
-#pragma unroll
-                for (int pr = kQkPairs + (NP - kQkPairs) * i / H; pr < kQkPairs + (NP - kQkPairs) * (i + 1) / H; ++pr)
-                    weight_pair(sc, mu, pr, pb);
-            } else {
-#pragma unroll
-                for (int pr = NP * (i - H) / H; pr < NP * (i - H + 1) / H; ++pr) pair_sum(pb, pr, part);
-            }
             if (i == 1) mid();
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_setprio(0);
+    };
+    // The weights of a tile (scores s) into pb and their row sums into lsum.  A tile whose
+    // sums are not finite or above 2^64 (a score far above its row's reference) flags the
+    // unit to be computed again against exact row maxima.
+    auto weights = [&](const f32x16_t (&s)[RB], bf16x8_t (&pb)[RB][2]) {
+        float part[RB][2];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) part[rb][0] = part[rb][1] = 0.f;
+#pragma unroll
+        for (int pr = 0; pr < NP; ++pr) weight_pair(s, m_ref, pr, pb);
+#pragma unroll
+        for (int pr = 0; pr < NP; ++pr) pair_sum(pb, pr, part);
         bool over = false;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -676,6 +660,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         uint32_t idq_next; // those of [t0+8, t0+12), loaded during the trip
         TileRsrc rs3;      // descriptors of the loads of tile t+3 at step t
         f32x16_t sa[RB], sb[RB];
+        bf16x8_t pbuf[RB][2];  // weights of the tile whose P V comes next
         // scores are read by vector instructions: keep them in vector registers
         auto pin_s = [&](f32x16_t (&s)[RB]) {
 #pragma unroll
@@ -708,13 +693,23 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) m_ref[rb] = 0.f;
             }
+            if constexpr (!MAX_ONLY) {
+                // the weights of tile t_lo, for the first step's P V
+                if (t_lo < t_end) {
+                    if (!set_refs && need_mask(t_lo, okq & 3u)) mask(t_lo, sa, okq & 3u);
+                    weights(sa, pbuf);
+                }
+            }
         }
-        // Step t (the ST-th of its loop trip): tile t in stage ST, its scores in sc; tile
-        // t+1's go to sn.  The loads of tile t+3 (descriptors made at step t-1) are issued
-        // between the score products, the descriptors of tile t+4 made between the P V
-        // products; the first step of a trip loads the block ids of the trip after next.
-        // A step issues 2 NIK loads, the first of a trip one more (after its tile loads),
-        // which fixes how many of them the next step's wait leaves in flight.
+        // Step t (the ST-th of its loop trip): tile t in stage ST; tile t+1's scores go to
+        // sn.  The attention pass runs the products (tile t+1's scores, tile t's P V with
+        // the weights pbuf made the step before), then tile t+1's weights into pbuf; the
+        // max-only pass takes the maxima of tile t's scores (sc) and computes tile t+1's.
+        // The loads of tile t+3 (descriptors made at step t-1) are issued between the
+        // score products, the descriptors of tile t+4 made between the P V products; the
+        // first step of a trip loads the block ids of the trip after next.  A step issues
+        // 2 NIK loads, the first of a trip one more (after its tile loads), which fixes how
+        // many of them the next step's wait leaves in flight.
         auto step = [&](auto st, int t, f32x16_t (&sc)[RB], f32x16_t (&sn)[RB]) {
             constexpr int ST = decltype(st)::value;
             wait_loads_and_barrier<2 * NIK + (ST == 1 && kPaged ? 1 : 0)>();
@@ -731,7 +726,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                 if constexpr (ST == 0) idq_next = load_idq(t + 8);
             }
             if (t < t_end) {
-                if (need_mask(t, okq & 3u)) mask(t, sc, okq & 3u);
+                if (MAX_ONLY && need_mask(t, okq & 3u)) mask(t, sc, okq & 3u);
                 if constexpr (MAX_ONLY) {
                     float mx[RB];
                     tile_max(sc, mx);
@@ -740,14 +735,17 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                     qk(Stage<(ST + 1) % 4>{}, sn);
                     next_desc();
                 } else {
-                    bf16x8_t pb[RB][2];
-                    float mu[RB];
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) mu[rb] = m_ref[rb];
-                    qk_softmax(Stage<(ST + 1) % 4>{}, sc, sn, mu, pb, lst, rs);
+                    // tile t's weights were made at the end of the step before (or the prologue)
+                    __builtin_amdgcn_s_setprio(1);
+                    products(Stage<(ST + 1) % 4>{}, Stage<ST>{}, sn, pbuf, lst, rs, next_desc);
                     if constexpr (ST == 0) idq_next = load_idq(t + 8);
-                    pv(Stage<ST>{}, sc, mu, pb, next_desc);
+                    __builtin_amdgcn_s_setprio(0);
                     pin_acc();
+                    if (t + 1 < t_end) {
+                        const uint32_t ok1 = (okq >> 2) & 3u;  // page bits of tile t+1
+                        if (need_mask(t + 1, ok1)) mask(t + 1, sn, ok1);
+                        weights(sn, pbuf);
+                    }
                 }
                 // (placed after the products, so that it does not split the stretch above)
                 pin_s(sn);
