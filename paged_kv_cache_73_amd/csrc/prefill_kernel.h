@@ -68,6 +68,13 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, const ui
         rsrc, (__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(dst)), 16, voffset, 0, 0, 0);
 }
 
+// 4 bytes per lane: lane l's bytes land at dst + 4 l
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rsrc, const uint16_t* dst,
+                                          int32_t voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(dst)), 4, voffset, 0, 0, 0);
+}
+
 __device__ __forceinline__ lds_v4_ptr_t to_lds_v4(const uint16_t* p) {
     return (lds_v4_ptr_t)(const_cast<uint16_t*>(p));
 }
@@ -78,6 +85,12 @@ __device__ __forceinline__ lds_v4_ptr_t to_lds_v4(const uint16_t* p) {
 // every wave's.  The compiler's own barrier would first wait for every load in flight;
 // this one keeps the later stages' loads flying.  (The memory clobber keeps LDS accesses
 // on their side of it.)
+// A barrier after this wave's LDS accesses only: loads from memory may stay in flight
+// (the workgroup barrier of the language waits for them too).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_loads_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -93,7 +106,8 @@ constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr int kPrefillStages = 4;                         // LDS tile buffers
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X
 constexpr float kFastSumLimit = 18446744073709551616.f;  // 2^64: weights of a tile on the fast path
-constexpr int kMaxRankedRequests = 256;  // requests ordered by key count in-kernel
+constexpr int kMaxRankedRequests = 256;
+constexpr int64_t kQPrefetchBytes = 3 << 20;  // at most this much of q per XCD is pulled into L2 at the start  // requests ordered by key count in-kernel
 // Jobs per XCD ordered by key tiles in-kernel.  Ranking costs O(jobs^2) LDS compares per
 // workgroup and separates the query tiles of a group (which then stop sharing K/V pages
 // in L2); past a few jobs per workgroup slot the batch order, which keeps a group's tiles
@@ -179,11 +193,51 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const int batch = n_groups / num_kv_heads;
     // work units per XCD: jobs, each cut into n_split key ranges when splitting
     const int n_jobs = (n_groups + kXcds - 1) / kXcds * n_qtiles * n_split;
+    // cu_q and cu_k of up to kMaxRankedRequests requests are read into LDS once, by one
+    // round of loads, for the orders and for every unit's bounds
+    __shared__ int32_t cuq_s[kMaxRankedRequests + 1], cuk_s[kMaxRankedRequests + 1];
+    const bool cu_lds = batch <= kMaxRankedRequests;
+    if (cu_lds) {
+        for (int j = tid; j <= batch; j += kPrefillThreads) {
+            cuq_s[j] = cu_q[j];
+            cuk_s[j] = cu_k[j];
+        }
+        __syncthreads();
+    }
+    // While the orders below are worked out, the workgroups of an XCD pull the q rows that
+    // XCD will read into its L2, one 128-byte line per lane: with a multiple of 8 KV heads,
+    // XCD x serves KV heads x, x+8, ... whatever the request order.  The loads go straight
+    // to LDS, into this wave's slice of the last V stage, which nothing reads before this
+    // wave's own tile loads (later, in order) overwrite it.
+    if (cu_lds && num_kv_heads % kXcds == 0) {
+        constexpr int kLines = G * D * 2 / 128;  // lines of one token's q rows of one KV head
+        const int hpx = num_kv_heads / kXcds;    // KV heads per XCD
+        const int sum_q = cuq_s[batch];
+        const int64_t lines = static_cast<int64_t>(sum_q) * hpx * kLines;
+        if (lines * 128 <= kQPrefetchBytes) {
+            const int64_t q_bytes = static_cast<int64_t>(sum_q) * num_heads * D * 2;
+            const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(q), 0, static_cast<int32_t>(min(q_bytes, static_cast<int64_t>(INT32_MAX))),
+                kBufferDword3);
+            const int per = n_slots * kPrefillThreads;  // lanes of the XCD
+            for (int64_t l0 = 0; l0 < lines; l0 += per) {  // (uniform trip count)
+                const int64_t line = l0 + slot * kPrefillThreads + tid;
+                int32_t off = INT32_MIN;  // past the bound: no load
+                if (line < lines) {
+                    const int64_t c = line / kLines;
+                    const int token = static_cast<int>(c / hpx), hkv = xcd + kXcds * static_cast<int>(c % hpx);
+                    const int64_t o = (static_cast<int64_t>(token) * num_heads + hkv * G) * D * 2 + (line % kLines) * 128;
+                    off = o < INT32_MAX ? static_cast<int32_t>(o) : INT32_MIN;
+                }
+                load_lds4(qrs, v_st3 + (kPrefillKeys / kPrefillWaves) * (tid / kWave) * D, off);
+            }
+        }
+    }
     // key tiles of a job: -1 when its first token is past the request's queries
     auto job_tiles = [&](int req, int tok0) {
-        const int q_len = cu_q[req + 1] - cu_q[req];
+        const int q_len = cuq_s[req + 1] - cuq_s[req];  // (the orders are worked out from LDS only)
         if (tok0 >= q_len) return -1;
-        const int k_len_req = cu_k[req + 1] - cu_k[req];
+        const int k_len_req = cuk_s[req + 1] - cuk_s[req];
         const int k_len = kPaged ? min(k_len_req, max_blocks * BS) : k_len_req;
         const int tok_last = min(tok0 + TOK, q_len) - 1;
         const int kv_end = causal ? min(k_len, k_len_req - q_len + tok_last + 1) : k_len;
@@ -196,15 +250,15 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         if (s >= parts) return -1;
         return parts == 1 ? tiles : (s == parts - 1 ? tiles - s * split_tiles : split_tiles);
     };
-    const bool rank_requests = batch > 1 && batch <= kMaxRankedRequests;
-    const bool rank_jobs = n_jobs > 1 && n_jobs <= kMaxRankedJobs;
+    const bool rank_requests = cu_lds && batch > 1;
+    const bool rank_jobs = cu_lds && n_jobs > 1 && n_jobs <= kMaxRankedJobs;
     int32_t* const klen = reinterpret_cast<int32_t*>(k_st0);  // key count of each request
     int32_t* const jobs = klen + kMaxRankedRequests;             // sort key of each unit
     if (rank_requests) {
         const int padded = (batch + 3) & ~3;  // whole 16-byte reads; -1 pads (below any count)
         for (int j = tid; j < padded; j += kPrefillThreads)
-            klen[j] = j < batch ? cu_k[j + 1] - cu_k[j] : -1;
-        __syncthreads();
+            klen[j] = j < batch ? cuk_s[j + 1] - cuk_s[j] : -1;
+        lds_barrier();
         const int4* const klen4 = reinterpret_cast<const int4*>(klen);
         for (int j = tid; j < batch; j += kPrefillThreads) {
             const int kj = klen[j];
@@ -219,7 +273,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             }
             perm[ahead] = j;
         }
-        __syncthreads();
+        lds_barrier();
     }
     auto request_of = [&](int rank) { return rank_requests ? perm[rank] : rank; };
     if (rank_jobs) {
@@ -241,7 +295,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             }
             jobs[c] = key;
         }
-        __syncthreads();
+        lds_barrier();
         const int4* const jobs4 = reinterpret_cast<const int4*>(jobs);
         for (int c = tid; c < n_jobs; c += kPrefillThreads) {
             const int32_t v = jobs[c];
@@ -253,7 +307,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             }
             order[ahead] = c;
         }
-        __syncthreads();  // (the scratch tables in the first K stage are free after this)
+        lds_barrier();  // (the scratch tables in the first K stage are free after this)
     }
 
     auto run_unit = [&](int c) {
@@ -266,11 +320,23 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     if (group >= n_groups) return;  // uniform: grid padding
     const int hkv = group % num_kv_heads;
     const int req = __builtin_amdgcn_readfirstlane(request_of(group / num_kv_heads));  // scalar addressing
-    const int q0 = cu_q[req];
-    const int q_len = cu_q[req + 1] - q0;
+    // the request's bounds from LDS (past kMaxRankedRequests requests this unit's four
+    // values are copied there first: every read of them is then an LDS read)
+    int ci = req;
+    if (!cu_lds) {
+        if (tid == 0) {
+            cuq_s[0] = cu_q[req], cuq_s[1] = cu_q[req + 1];
+            cuk_s[0] = cu_k[req], cuk_s[1] = cu_k[req + 1];
+        }
+        __syncthreads();  // (the unit before ended with a barrier after its last read)
+        ci = 0;
+    }
+    const int q0 = __builtin_amdgcn_readfirstlane(cuq_s[ci]);
+    const int k0_req = __builtin_amdgcn_readfirstlane(cuk_s[ci]);
+    const int q_len = __builtin_amdgcn_readfirstlane(cuq_s[ci + 1]) - q0;
     const int tok0 = qtile * TOK;
     if (tok0 >= q_len) return;  // uniform: tile past this request's queries
-    const int k_len_req = cu_k[req + 1] - cu_k[req];
+    const int k_len_req = __builtin_amdgcn_readfirstlane(cuk_s[ci + 1]) - k0_req;
     const int cached = k_len_req - q_len;                       // may be negative
     const int k_len = kPaged ? min(k_len_req, max_blocks * BS) : k_len_req;  // keys past the table: never read
     const int tok_last = min(tok0 + TOK, q_len) - 1;
@@ -342,7 +408,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     }
 
     const int32_t* table_row = kPaged ? block_table + static_cast<int64_t>(req) * max_blocks : nullptr;
-    const int64_t key_base = kPaged ? 0 : cu_k[req];  // first packed row of the request (contiguous)
+    const int64_t key_base = kPaged ? 0 : k0_req;  // first packed row of the request (contiguous)
     const int32_t row_stride = num_kv_heads * D * 2;  // bytes per slot
 
     // ---- loader ---------------------------------------------------------------------
