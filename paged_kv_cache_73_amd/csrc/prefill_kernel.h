@@ -234,10 +234,12 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         }
     }
     // key tiles of a job: -1 when its first token is past the request's queries
-    auto job_tiles = [&](int req, int tok0) {
-        const int q_len = cuq_s[req + 1] - cuq_s[req];  // (the orders are worked out from LDS only)
+    // (cq, ck: the LDS copies of cu_q, cu_k, or the global arrays past kMaxRankedRequests
+    // requests; each kind of call is its own loop, so no read goes through a generic pointer)
+    auto job_tiles = [&](const auto* cq, const auto* ck, int req, int tok0) {
+        const int q_len = cq[req + 1] - cq[req];
         if (tok0 >= q_len) return -1;
-        const int k_len_req = cuk_s[req + 1] - cuk_s[req];
+        const int k_len_req = ck[req + 1] - ck[req];
         const int k_len = kPaged ? min(k_len_req, max_blocks * BS) : k_len_req;
         const int tok_last = min(tok0 + TOK, q_len) - 1;
         const int kv_end = causal ? min(k_len, k_len_req - q_len + tok_last + 1) : k_len;
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         return parts == 1 ? tiles : (s == parts - 1 ? tiles - s * split_tiles : split_tiles);
     };
     const bool rank_requests = cu_lds && batch > 1;
-    const bool rank_jobs = cu_lds && n_jobs > 1 && n_jobs <= kMaxRankedJobs;
+    const bool rank_jobs = n_jobs > 1 && n_jobs <= kMaxRankedJobs;
     int32_t* const klen = reinterpret_cast<int32_t*>(k_st0);  // key count of each request
     int32_t* const jobs = klen + kMaxRankedRequests;             // sort key of each unit
     if (rank_requests) {
@@ -284,16 +286,21 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         // index.  The rank of unit c is the number of larger keys; the table is padded
         // with zeros (below every key) to whole 16-byte reads.
         const int padded = (n_jobs + 3) & ~3;
-        for (int c = tid; c < padded; c += kPrefillThreads) {
+        auto job_key = [&](int c, const auto* cq, const auto* ck) {
             int32_t key = 0;
             if (c < n_jobs) {
                 const int job = c / n_split;
                 const int g = (job / n_qtiles) * kXcds + xcd;
-                const int tiles = g < n_groups ? job_tiles(request_of(g / num_kv_heads), (job % n_qtiles) * TOK) : -1;
+                const int tiles = g < n_groups ? job_tiles(cq, ck, request_of(g / num_kv_heads), (job % n_qtiles) * TOK) : -1;
                 const int ut = unit_tiles(tiles, c % n_split);
                 key = (min(ut + 1, 0x7FFE) << 16) | (0xFFFF - c);
             }
-            jobs[c] = key;
+            return key;
+        };
+        if (cu_lds) {
+            for (int c = tid; c < padded; c += kPrefillThreads) jobs[c] = job_key(c, cuq_s, cuk_s);
+        } else {
+            for (int c = tid; c < padded; c += kPrefillThreads) jobs[c] = job_key(c, cu_q, cu_k);
         }
         lds_barrier();
         const int4* const jobs4 = reinterpret_cast<const int4*>(jobs);

@@ -508,15 +508,15 @@ def test_contiguous_prefill_full_size():
 
 
 @pytest.mark.parametrize("batch,q_hi,num_heads,num_kv_heads", [
-    (300, 3, 4, 2),     # requests in batch order, jobs ranked (75 jobs per XCD)
-    (2400, 3, 4, 2),    # requests in batch order, jobs ranked (600 per XCD)
+    (300, 3, 4, 2),     # requests in batch order (bounds read from memory), jobs ranked (75 per XCD)
+    (2400, 3, 4, 2),    # requests in batch order, jobs in group order (600 per XCD)
     (2400, 100, 4, 2),  # both in batch order (1200 jobs per XCD)
-    (256, 320, 16, 8),  # requests ranked, jobs in group order (1280 jobs per XCD)
+    (256, 320, 16, 8),  # requests ranked (bounds in LDS), jobs in group order (1280 per XCD)
 ])
 def test_prefill_many_requests(batch, q_hi, num_heads, num_kv_heads):
-    # The kernel ranks requests by key count up to 256 requests and the jobs of an XCD by
-    # key tiles up to 1024 jobs; past either limit it keeps the batch / group order.  Every
-    # order must give the same rows.
+    # The kernel ranks requests by key count up to 256 requests (their bounds then sit in
+    # LDS) and the jobs of an XCD by key tiles up to 384 jobs; past either limit it keeps
+    # the batch / group order.  Every order must give the same rows.
     rng = random.Random(batch * 1000 + q_hi)
     new = [rng.randint(1, q_hi) for _ in range(batch)]
     cached = [rng.randint(0, 40) for _ in range(batch)]
