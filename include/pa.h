@@ -316,8 +316,8 @@ int pa_prefill_varlen_contiguous(void* out, const void* q, const void* k, const 
 /* ---------------------------------------------------------------------------------
  * Measurement helper (not part of the attention path): reads `bytes` (a multiple of 16)
  * of device memory at `buf` with non-temporal 16-byte loads from `grid` workgroups of
- * 256 threads, as a plain streaming read; `sink` is a device word that is normally
- * left untouched.  Timing it gives the attainable HBM read bandwidth that the decode
+ * 256 threads, each reading its own contiguous stretch, as a plain streaming read;
+ * `sink` is a device word that is normally left untouched.  Timing it gives the attainable HBM read bandwidth that the decode
  * kernel is compared with.
  * ------------------------------------------------------------------------------- */
 int pa_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream);
