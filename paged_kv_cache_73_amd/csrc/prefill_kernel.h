@@ -177,7 +177,9 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // handed to the XCDs round-robin), and the jobs of group g all run on XCD g % 8: the
     // query tiles of a group read the same K/V pages, which then stay in that XCD's L2.
     // Requests are ranked by key count, longest first, and group g belongs to the
-    // request of rank g / Hkv, so that every request's heads are spread over the 8 XCDs.
+    // request of rank g / Hkv, so that every request's heads are spread over the 8 XCDs
+    // (with a multiple of 8 KV heads they are whatever the order, and when the units are
+    // ranked the requests are not).
     // The grid holds n_slots workgroups per XCD (no more than can run at once), each of
     // which runs a list of its XCD's units: they are ranked by key tiles, longest first,
     // and dealt to the slots in snake order (round k gives rank kS + s, or kS + S-1-s in
@@ -252,8 +254,10 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         if (s >= parts) return -1;
         return parts == 1 ? tiles : (s == parts - 1 ? tiles - s * split_tiles : split_tiles);
     };
-    const bool rank_requests = cu_lds && batch > 1;
     const bool rank_jobs = n_jobs > 1 && n_jobs <= kMaxRankedJobs;
+    // (with a multiple of 8 KV heads, XCD x serves heads x, x+8, ... of every request
+    // whatever their order, and the job order alone makes the schedule: no request order)
+    const bool rank_requests = cu_lds && batch > 1 && !(rank_jobs && num_kv_heads % kXcds == 0);
     int32_t* const klen = reinterpret_cast<int32_t*>(k_st0);  // key count of each request
     int32_t* const jobs = klen + kMaxRankedRequests;             // sort key of each unit
     if (rank_requests) {
@@ -303,16 +307,22 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             for (int c = tid; c < padded; c += kPrefillThreads) jobs[c] = job_key(c, cu_q, cu_k);
         }
         lds_barrier();
+        // tpj neighbouring lanes count the larger keys of one unit, each over a share of
+        // the table, and add their counts
         const int4* const jobs4 = reinterpret_cast<const int4*>(jobs);
-        for (int c = tid; c < n_jobs; c += kPrefillThreads) {
+        const int tpj = n_jobs <= kPrefillThreads / 4 ? 4 : n_jobs <= kPrefillThreads / 2 ? 2 : 1;
+        const int sub = tid % tpj;
+        for (int c = tid / tpj; c < n_jobs; c += kPrefillThreads / tpj) {
             const int32_t v = jobs[c];
             int ahead = 0;
 #pragma unroll 4
-            for (int i = 0; i < padded / 4; ++i) {
+            for (int i = sub; i < padded / 4; i += tpj) {
                 const int4 u = jobs4[i];
                 ahead += (u.x > v) + (u.y > v) + (u.z > v) + (u.w > v);
             }
-            order[ahead] = c;
+            if (tpj > 1) ahead += __shfl_xor(ahead, 1);
+            if (tpj > 2) ahead += __shfl_xor(ahead, 2);
+            if (sub == 0) order[ahead] = c;
         }
         lds_barrier();  // (the scratch tables in the first K stage are free after this)
     }
