@@ -30,11 +30,16 @@
 //   address is a scalar; loads bounded to the slice's valid keys return zeros past kv_end
 //   and for a block id outside the pool, so masked keys never bring NaN into a product.
 //   Masking sets scores past a row's limit (and of unassigned blocks) to -inf.
-// * Software pipeline, one barrier per tile: while the products of tile t+1's scores run,
-//   the wave computes tile t's weights on the vector unit (the two are independent, and
-//   one wave issues vector instructions while its matrix products execute), then the
-//   products of tile t's P V.  Four LDS stages: t (V read), t+1 (K read), and the loads
-//   of t+2 and t+3 in flight, two steps ahead of their use.
+// * Software pipeline, one barrier per tile, each step in two phases: the step's 16
+//   products back to back at raised wave priority (tile t+1's scores, then tile t's P V
+//   with the weights made the step before), then tile t+1's weights on the vector unit at
+//   normal priority.  The other wave of the SIMD (another workgroup) runs its products
+//   while this one does its vector work, and the matrix core they share makes them take
+//   turns.  Four LDS stages: t (V read), t+1 (K read), and the loads of t+2 and t+3 in
+//   flight, two steps ahead of their use.
+// * The start of a launch: cu_seqlens go to LDS once, the workgroups work out the same
+//   orders of requests and units (longest first) there, and meanwhile pull the q rows
+//   of their XCD into its L2.
 // * Weights without a per-tile maximum: p = 2^(s*scale*log2e - m) against the row's
 //   reference m, the row's maximum over the unit's first tile.  The quotient
 //   sum(p v) / sum(p) does not depend on m; a tile whose weights sum past 2^64 sends the
