@@ -924,6 +924,9 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         if (rank >= n_jobs) break;  // (the last round: no later one)
         run_unit(rank_jobs ? order[rank] : rank);
     }
+    // a workgroup whose units all turned out empty still has its q-row loads into LDS in
+    // flight: they land before the wave ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace pa
