@@ -118,6 +118,12 @@ constexpr int64_t kQPrefetchBytes = 3 << 20;  // at most this much of q per XCD 
 // in L2); past a few jobs per workgroup slot the batch order, which keeps a group's tiles
 // together, measured faster.
 constexpr int kMaxRankedJobs = 384;
+// Most workgroups per XCD whose lists are placed on the CUs by their load (below); a
+// larger grid keeps the plain deal.
+constexpr int kMaxPlacedSlots = 64;
+// What starting a unit costs its slot, in key tiles (its first loads, q rows, the store):
+// ~2 us against ~1 us per tile when two workgroups share a CU.
+constexpr int kUnitCostTiles = 2;
 
 // Key ranges of a job of `tiles` key tiles when jobs are cut into ranges of split_tiles
 // tiles, at most n_split of them (the last one takes the rest).
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     uint16_t* __restrict__ out, int32_t num_heads, int32_t num_kv_heads, int32_t num_blocks,
     int32_t max_blocks, float qscale, int32_t causal, int32_t n_qtiles, int32_t n_groups,
     int32_t n_split_arg, int32_t split_tiles_arg, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, int32_t n_slots) {
+    float2* __restrict__ part_ml, int32_t n_slots, int32_t cus_per_xcd) {
     const int n_split = kSplit ? n_split_arg : 1;
     const int split_tiles = kSplit ? split_tiles_arg : 0;
     constexpr int BN = kPrefillKeys;
@@ -171,8 +177,8 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
         if constexpr (S == 0) return v_st0; else if constexpr (S == 1) return v_st1;
         else if constexpr (S == 2) return v_st2; else return v_st3;
     };
-    static_assert((kMaxRankedRequests + kMaxRankedJobs) * 4 <= TILE * 2,
-                  "the ranking's scratch tables fit in the first K stage");
+    static_assert((kMaxRankedRequests + kMaxRankedJobs) * 4 <= TILE * 2 && kMaxRankedJobs * 4 <= TILE * 2,
+                  "the ranking's scratch tables fit in the first two K stages");
     __shared__ int32_t perm[kMaxRankedRequests];   // request of each rank
     __shared__ int32_t order[kMaxRankedJobs];      // this XCD's work unit of each rank
     __shared__ int32_t redo;
@@ -187,10 +193,11 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // ranked the requests are not).
     // The grid holds n_slots workgroups per XCD (no more than can run at once), each of
     // which runs a list of its XCD's units: they are ranked by key tiles, longest first,
-    // and dealt to the slots in snake order (round k gives rank kS + s, or kS + S-1-s in
-    // odd rounds, to slot s), so that the long units start first and each slot's short
-    // ones balance its long ones.  Workgroups started by the hardware as others end would
-    // wait for a slot on their own XCD; these never wait.  Every workgroup derives the
+    // and dealt to S lists in snake order (round k gives rank kS + v, or kS + S-1-v in
+    // odd rounds, to list v), so that the long units start first and each list's short
+    // ones balance its long ones; the lists are then placed on the CUs by their load.
+    // Workgroups started by the hardware as others end would wait for a slot on their own
+    // XCD; these never wait.  Every workgroup derives the
     // same orders from cu_q / cu_k in LDS; beyond kMaxRankedRequests requests or
     // kMaxRankedJobs units per XCD the batch order is kept instead.
     const int L = blockIdx.x;
@@ -265,6 +272,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     const bool rank_requests = cu_lds && batch > 1 && !(rank_jobs && num_kv_heads % kXcds == 0);
     int32_t* const klen = reinterpret_cast<int32_t*>(k_st0);  // key count of each request
     int32_t* const jobs = klen + kMaxRankedRequests;             // sort key of each unit
+    int32_t* const rtiles = reinterpret_cast<int32_t*>(k_st1);   // key tiles of each rank
     if (rank_requests) {
         const int padded = (batch + 3) & ~3;  // whole 16-byte reads; -1 pads (below any count)
         for (int j = tid; j < padded; j += kPrefillThreads)
@@ -327,10 +335,78 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             }
             if (tpj > 1) ahead += __shfl_xor(ahead, 1);
             if (tpj > 2) ahead += __shfl_xor(ahead, 2);
-            if (sub == 0) order[ahead] = c;
+            if (sub == 0) {
+                order[ahead] = c;
+                rtiles[ahead] = (v >> 16) - 1;  // -1: no unit
+            }
         }
-        lds_barrier();  // (the scratch tables in the first K stage are free after this)
+        lds_barrier();
     }
+    // Placement of the lists on the CUs.  The deal above makes n_slots lists (list v: ranks
+    // kS + v in even rounds k, kS + S-1-v in odd ones); which workgroup runs which list
+    // decides which lists share a CU.  The hardware puts workgroup slot s of an XCD on CU
+    // s mod C (C its CUs) on the first pass and slot s + C on the same CU on the second,
+    // and two workgroups on one CU share its SIMDs: each runs ~1 us per key tile while both
+    // are busy, ~0.75 us alone.  A CU's end is then set by its heavier list, which runs
+    // alone once the lighter one is done, so the heaviest lists get CUs of their own (when
+    // there are fewer than 2C slots) and each remaining CU pairs the heaviest list left with
+    // the lightest (the heavier on the first-pass slot, whose waves are older and win ties
+    // for the SIMD).  Only the speed depends on where a workgroup actually runs: every list
+    // is run by exactly one workgroup whatever the placement.
+    int list = slot;
+    if (rank_jobs && cus_per_xcd > 0 && n_slots > cus_per_xcd && n_slots <= 2 * cus_per_xcd &&
+        n_slots <= kMaxPlacedSlots) {
+        // Every wave computes the load of each list (lane v: list v, the key tiles of its
+        // units and kUnitCostTiles per unit) into a table of its own; the four waves then
+        // rank a quarter of the lists each (four lanes per list, each against a quarter of
+        // the table) into the shared table of lists by load rank.
+        static_assert(kMaxPlacedSlots == kWave && kMaxPlacedSlots == 16 * kPrefillWaves,
+                      "a list per lane; 16 lists ranked per wave");
+        __shared__ __align__(16) int32_t vkeys[kPrefillWaves][kMaxPlacedSlots];
+        __shared__ int32_t by_load[kMaxPlacedSlots];
+        const int v = tid % kWave;
+        const int wv = tid / kWave;
+        int32_t* const vkey = vkeys[wv];
+        int load = 0;
+        if (v < n_slots) {
+            const int r0 = v, r1 = 2 * n_slots - 1 - v;  // the first two rounds
+            const int t0 = r0 < n_jobs ? rtiles[r0] : -1, t1 = r1 < n_jobs ? rtiles[r1] : -1;
+            load = (t0 >= 0 ? t0 + kUnitCostTiles : 0) + (t1 >= 0 ? t1 + kUnitCostTiles : 0);
+            for (int k = 2;; ++k) {
+                const int rank = k * n_slots + (k % 2 == 0 ? v : n_slots - 1 - v);
+                if (rank >= n_jobs) break;
+                const int tiles = rtiles[rank];
+                if (tiles >= 0) load += tiles + kUnitCostTiles;
+            }
+        }
+        // distinct keys, a larger one meaning "heavier": more load, or as much and a lower
+        // index (-1 past the lists: below all)
+        vkey[v] = v < n_slots ? (min(load, (1 << 23) - 1) << 7) | (kMaxPlacedSlots - 1 - v) : -1;
+        // (a wave reads its own LDS writes in order; the asm keeps the compiler from waiting
+        // here for the q-row loads into the last V stage, which do not touch this table)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int list_r = 16 * wv + v / 4, sub = v % 4;
+        const int32_t kr = vkey[list_r];
+        const int4* const part = reinterpret_cast<const int4*>(vkey) + 4 * sub;
+        int heavier = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int4 u = part[i];
+            heavier += (u.x > kr) + (u.y > kr) + (u.z > kr) + (u.w > kr);
+        }
+        heavier += __builtin_amdgcn_update_dpp(0, heavier, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+        heavier += __builtin_amdgcn_update_dpp(0, heavier, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+        if (sub == 0 && list_r < n_slots) by_load[heavier] = list_r;
+        lds_barrier();
+        const int n_pairs = n_slots - cus_per_xcd;  // CUs running two workgroups of this XCD
+        const int n_solo = cus_per_xcd - n_pairs;   // CUs running one
+        const int load_rank = slot < n_pairs ? n_solo + slot                          // first pass, paired
+                            : slot < cus_per_xcd ? slot - n_pairs                     // alone on its CU
+                            : n_slots - 1 - (slot - cus_per_xcd);                     // second pass
+        list = by_load[load_rank];
+    }
+    // (the scratch tables in the first two K stages are free once every wave is past the first
+    // barrier of its first unit)
 
     auto run_unit = [&](int c) {
     const int job = c / n_split;
@@ -918,9 +994,9 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     }
     };  // run_unit
 
-    // this slot's units, dealt in snake order from the XCD's ranking
+    // this workgroup's units: those of its list, dealt in snake order from the XCD's ranking
     for (int k = 0;; ++k) {
-        const int rank = k * n_slots + (k % 2 == 0 ? slot : n_slots - 1 - slot);
+        const int rank = k * n_slots + (k % 2 == 0 ? list : n_slots - 1 - list);
         if (rank >= n_jobs) break;  // (the last round: no later one)
         run_unit(rank_jobs ? order[rank] : rank);
     }

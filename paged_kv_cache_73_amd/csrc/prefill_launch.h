@@ -139,6 +139,7 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
     const int64_t per_xcd = (n_groups + kXcds - 1) / kXcds * n_qtiles * sp.n_split;  // work units
     if (per_xcd * kXcds > INT32_MAX) return PA_ERR_UNSUPPORTED;
     const int32_t n_slots = static_cast<int32_t>(std::max<int64_t>(1, std::min(per_xcd, prefill_slots() / kXcds)));
+    const int32_t cus_per_xcd = static_cast<int32_t>(prefill_slots() / (2 * kXcds));
     float* part_o = sp.n_split > 1 ? static_cast<float*>(workspace) : nullptr;
     float2* part_ml = sp.n_split > 1
         ? reinterpret_cast<float2*>(part_o + static_cast<size_t>(sp.units) * kPrefillRows * D) : nullptr;
@@ -152,7 +153,7 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                            static_cast<uint16_t*>(out), num_heads, kv.num_kv_heads,
                            kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
                            static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups),
-                           sp.n_split, sp.split_tiles, part_o, part_ml, n_slots);
+                           sp.n_split, sp.split_tiles, part_o, part_ml, n_slots, cus_per_xcd);
     else
         hipLaunchKernelGGL((prefill_kernel<D, G, BS, false>), grid, dim3(kPrefillThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const char*>(kv.k),
@@ -160,7 +161,7 @@ int launch_prefill(const KvSource& kv, void* out, const void* q, int32_t batch,
                            static_cast<uint16_t*>(out), num_heads, kv.num_kv_heads,
                            kv.num_blocks, kv.max_blocks, scale * kLog2e, causal,
                            static_cast<int32_t>(n_qtiles), static_cast<int32_t>(n_groups), 1, 0,
-                           nullptr, nullptr, n_slots);
+                           nullptr, nullptr, n_slots, cus_per_xcd);
     if (sp.n_split > 1 && (passes & kPass2)) {
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
         // workgroups per job: the rows of the tokens a query tile can hold (one token per
