@@ -979,8 +979,18 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
             continue;
         }
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        if (!row_ok[rb]) continue;
-        uint16_t* orow = out + (static_cast<int64_t>(q0 + tok[rb]) * num_heads + head[rb]) * D;
+        // The 32 rows of the block go through LDS, so that the stores write whole 16-byte
+        // pieces of a row, eight lanes per 128-byte line (a lane holds 8-byte pieces of 16
+        // rows' lines otherwise, and those partial writes held the end of a unit up by
+        // ~2 us).  Each wave uses its own K stage (every wave is past the key pass, whose
+        // last barrier ended all reads of the stages, and the next unit loads none before
+        // its first barrier); a wave reads its own LDS writes in order.  16-byte piece c
+        // of row x sits at position c ^ (x mod CH) of the row, which spreads both the
+        // writes and the row-wise reads over the banks.
+        constexpr int CH = D / 8;             // 16-byte pieces per row
+        constexpr int RPI = kWave / CH;       // rows per read instruction
+        static_assert(kPrefillWaves <= kPrefillStages && 32 * D <= TILE, "a K stage holds a wave's block");
+        uint16_t* const ost = w == 0 ? k_st0 : w == 1 ? k_st1 : w == 2 ? k_st2 : k_st3;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -989,8 +999,19 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
                               (static_cast<uint32_t>(to_bf16_bits(acc[rb][db][4 * i4 + 1] * inv)) << 16);
                 uint32_t hi = static_cast<uint32_t>(to_bf16_bits(acc[rb][db][4 * i4 + 2] * inv)) |
                               (static_cast<uint32_t>(to_bf16_bits(acc[rb][db][4 * i4 + 3] * inv)) << 16);
-                *reinterpret_cast<uint2*>(orow + 32 * db + 8 * i4 + 4 * h) = make_uint2(lo, hi);
+                const int c = 4 * db + i4;  // piece of d = 32db + 8i4 .. +8; half h of it
+                *reinterpret_cast<uint2*>(ost + r * D + 8 * (c ^ (r % CH)) + 4 * h) = make_uint2(lo, hi);
             }
+#pragma unroll
+        for (int kk = 0; kk < 32 / RPI; ++kk) {
+            const int x = RPI * kk + lane / CH, c = lane % CH;  // row x of the block, piece c
+            const uint4 v = *reinterpret_cast<const uint4*>(ost + x * D + 8 * (c ^ (x % CH)));
+            const int row = kWaveRows * w + 32 * rb + x;
+            const int tok_x = tok0 + row / G;
+            if (tok_x < q_len && (kAllRows || row < kUsedRows))
+                *reinterpret_cast<uint4*>(out + (static_cast<int64_t>(q0 + tok_x) * num_heads + hkv * G + row % G) * D +
+                                          8 * c) = v;
+        }
     }
     };  // run_unit
 
