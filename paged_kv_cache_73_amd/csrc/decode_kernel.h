@@ -145,14 +145,6 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     const int c = lane % LPR;   // 16-byte piece of the row
 
     const int32_t cap = max_blocks * BS;
-    // A plain decode step reads its table row b from page part * part_pages on: the ids of
-    // the first 64 pages go out together with the length (index clamped to the row; ids
-    // past the partition are never used), one trip to memory less before the first K/V
-    // loads.
-    const bool spec_ids = tm.cu_q == nullptr && !tm.contiguous && max_blocks > 0;  // uniform
-    int32_t spec_id = -1;
-    if (spec_ids)
-        spec_id = block_table[static_cast<int64_t>(b) * max_blocks + min(part * part_pages + lane, max_blocks - 1)];
     int32_t n_keys;
     int64_t row_index = b;  // block-table row
     int32_t first_block = 0;  // contiguous keys: the block (row) of key 0
@@ -324,8 +316,7 @@ __global__ __launch_bounds__(PA_DECODE_HPW * kWave) PA_DECODE_ATTR void decode_p
     for (int32_t pc = pg0; pc < pg1; pc += kWave) {
         const int np = (min(kWave, pg1 - pc) + VP - 1) / VP;  // (virtual) pages of the chunk
         const int32_t my_id = lane >= min(kWave, pg1 - pc) ? -1
-                              : tm.contiguous ? first_block + pc + lane
-                              : spec_ids && pc == pg0 ? spec_id : table_row[pc + lane];
+                              : tm.contiguous ? first_block + pc + lane : table_row[pc + lane];
         // id of step i: a scalar, or with small pages this lane's block
         auto step_id = [&](int i) -> int32_t {
             if constexpr (S::kSmall) return __shfl(my_id, i * VP + r0 / BS);
