@@ -525,6 +525,20 @@ def test_prefill_many_requests(batch, q_hi, num_heads, num_kv_heads):
     _run(w, requests=list(range(0, batch, 7)))
 
 
+@pytest.mark.parametrize("batch,q_max", [(3, 704), (4, 640), (7, 576)])
+def test_prefill_lists_placed_on_cus_some_alone(batch, q_max):
+    # With 8 KV heads an XCD runs `batch` groups of ceil(q_max / 64) query tiles: 33, 40
+    # and 63 ranked units, one list each, on an XCD of 32 CUs.  The kernel ranks the lists
+    # by load, gives the heaviest CUs of their own and pairs the rest heaviest with
+    # lightest; whatever the placement, every list must be run exactly once.  All rows.
+    rng = random.Random(batch * 100 + q_max)
+    new = [q_max] + [rng.randint(1, q_max) for _ in range(batch - 1)]
+    cached = [rng.randint(0, 2000) for _ in range(batch)]
+    w = W.prefill_workload(cached, new, num_heads=16, num_kv_heads=8, head_dim=128,
+                           block_size=16, seed=41)
+    _run(w)
+
+
 @pytest.mark.parametrize("per_key", [1.0, -1.0])
 def test_prefill_recompute_in_every_unit_of_a_workgroup(per_key):
     # Many small requests (about three jobs per workgroup slot, each workgroup running a
