@@ -39,7 +39,11 @@
 //   flight, two steps ahead of their use.
 // * The start of a launch: cu_seqlens go to LDS once, the workgroups work out the same
 //   orders of requests and units (longest first) there, and meanwhile pull the q rows
-//   of their XCD into its L2.
+//   of their XCD into its L2.  The unit lists are then placed on the CUs by load: two
+//   workgroups that share a CU share its SIMDs, so each CU pairs a heavy list with a
+//   light one.
+// * The end of a unit: O goes through LDS (a K stage per wave) so that the stores write
+//   whole 16-byte pieces of each output row.
 // * Weights without a per-tile maximum: p = 2^(s*scale*log2e - m) against the row's
 //   reference m, the row's maximum over the unit's first tile.  The quotient
 //   sum(p v) / sum(p) does not depend on m; a tile whose weights sum past 2^64 sends the
