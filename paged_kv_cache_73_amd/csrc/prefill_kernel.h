@@ -527,7 +527,6 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // masked can be NaN.
     constexpr int KPI = kWave * 16 / (2 * D);  // keys per load instruction: 4 (d 128), 8 (d 64)
     constexpr int NIK = SLICE / KPI;           // K (and V) load instructions per wave and tile
-    constexpr int NL = 2 * NIK + (kPaged ? 1 : 0);  // vector-memory instructions per wave and tile
     // chunk permutations.  K is read 16 keys x one chunk at a time (one chunk per lane):
     // those must fall in 16 different 16-byte bank groups.  V is read transposed, 4 keys
     // x 4 chunks at a time: the keys' 64 bytes must fall in different quarters of the
@@ -814,7 +813,8 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
     // wave computes tile t+1's scores (stage of t+1) and tile t's P V (stage of t), while
     // the loads of tiles t+2 and t+3 are in flight, so a load has two steps to land.
     // Step t starts by waiting for its own loads of tile t+1 (all but the last step's
-    // NL vector-memory instructions) and a barrier, after which tile t+1 is complete in
+    // vector-memory instructions: 2 NIK tile loads, and one block-id load on the first
+    // step of a loop trip when paged) and a barrier, after which tile t+1 is complete in
     // LDS and every wave is done with tile t-1's stage, into which tile t+3 is then
     // loaded.  The stage of a tile is fixed by its position in the unit, so the loop is
     // unrolled four times and every LDS address is static.  Both waves run every step
